@@ -1,0 +1,456 @@
+"""Pins for the CPU oracle (no GPU).
+
+The oracle is checked against things other than itself: hand-derived plans
+(tests/golden), closed-form counts, a brute-force token loop with math.exp,
+torch's fp64 scaled_dot_product_attention on dense masks, closed forms
+(Q = 0, constant V, common key offset, permutations), shift invariance of
+the softmax, and Cauchy-Schwarz for the bounds. Mutation tests plant
+plausible mistakes in the oracle (on the CPU) and check that a pin fails.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.fsattn_oracle as O
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _geom(t):
+    return oracle.MaskGeometry(*t)
+
+
+def _rand_qkv(rng, B, H, N, d, kscale=1.0):
+    q = rng.standard_normal((B, H, N, d))
+    k = kscale * rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, d))
+    return q, k, v
+
+
+# ------------------------------------------------------------------ plan
+
+def test_plan_matches_hand_derived_golden():
+    cases = json.load(open(os.path.join(GOLDEN, "plan_tiny.json")))["cases"]
+    for c in cases:
+        rp, ci = oracle.plan_bruteforce(_geom(c["mask"]))
+        assert rp.tolist() == c["row_ptr"], c["name"]
+        assert ci.tolist() == c["col_idx"], c["name"]
+
+
+def test_plan_sizes_of_workloads_match_hand_counts():
+    gold = {w["name"]: w for w in json.load(open(os.path.join(GOLDEN, "workload_plan_sizes.json")))["workloads"]}
+    for w in workloads.CONFIGS:
+        g = _geom(w.mask_tuple())
+        want = gold[w.name]
+        assert [len(oracle.live_frames(g, f)) for f in range(g.F)] == want["live_frames_per_frame"]
+        if g.N <= 20160:       # brute force at the larger sizes runs in the slow suite
+            rp, ci = oracle.plan_bruteforce(g)
+            assert len(rp) - 1 == want["num_q_blocks"]
+            assert len(ci) == want["nnz"]
+
+
+@pytest.mark.slow
+def test_plan_sizes_of_large_workloads_bruteforce():
+    gold = {w["name"]: w for w in json.load(open(os.path.join(GOLDEN, "workload_plan_sizes.json")))["workloads"]}
+    for w in workloads.CONFIGS:
+        g = _geom(w.mask_tuple())
+        rp, ci = oracle.plan_bruteforce(g)
+        assert len(ci) == gold[w.name]["nnz"]
+
+
+def test_plan_invariants_random_geometries():
+    rng = np.random.default_rng(7)
+    for _ in range(40):
+        T = 16 * int(rng.integers(1, 7))
+        divs = [b for b in range(16, T + 1, 16) if T % b == 0]
+        g = oracle.MaskGeometry(int(rng.integers(1, 8)), T, int(rng.integers(0, 4)), int(rng.integers(0, 4)),
+                                int(rng.integers(-1, 3)), int(rng.choice(divs)), int(rng.choice(divs)))
+        if g.r >= g.F:
+            g.r = -1
+        rp, ci = oracle.plan_bruteforce(g)
+        assert rp[0] == 0 and np.all(np.diff(rp) >= 1)     # every row sees its own frame
+        for qb in range(len(rp) - 1):
+            row = ci[rp[qb]:rp[qb + 1]]
+            assert np.all(np.diff(row) > 0)
+        # closed form: sum_f |L(f)| * (T/bq) * (T/bk)
+        nnz = sum(len(oracle.live_frames(g, f)) for f in range(g.F)) * (T // g.bq) * (T // g.bk)
+        assert len(ci) == nnz
+        # exhaustive token-level check: a listed block is all-live, an unlisted one all-masked
+        M = oracle.token_mask(g)
+        for qb in range(len(rp) - 1):
+            listed = set(ci[rp[qb]:rp[qb + 1]].tolist())
+            for kb in range(g.N // g.bk):
+                blk = M[qb * g.bq:(qb + 1) * g.bq, kb * g.bk:(kb + 1) * g.bk]
+                assert blk.all() if kb in listed else not blk.any()
+
+
+def test_invalid_geometry_rejected():
+    bad = [
+        (3, 48, 1, 1, 0, 32, 16),    # 32 does not divide 48
+        (3, 48, 1, 1, 0, 24, 16),    # 24 not a multiple of 16
+        (3, 48, 1, 1, 0, 0, 16),
+        (3, 48, -1, 1, 0, 16, 16),
+        (3, 48, 1, 1, 3, 16, 16),    # reference frame out of range
+        (3, 48, 1, 1, -2, 16, 16),
+    ]
+    for t in bad:
+        with pytest.raises(ValueError):
+            oracle.plan_bruteforce(_geom(t))
+
+
+def test_partial_block_count_under_coarse_tiles_hand_example():
+    # 2 frames x 48 tokens, block-diagonal mask, 32-token tiles over 96 tokens:
+    # live tiles (0,0) (0,1) (1,0) (1,1) (1,2) (2,1) (2,2); only (0,0) and (2,2) are full.
+    g = oracle.MaskGeometry(2, 48, 0, 0, -1, 16, 16)
+    assert oracle.partial_blocks_if_tiled(g, 32) == (5, 7)
+    # aligned tiles are never partial
+    assert oracle.partial_blocks_if_tiled(g, 48)[0] == 0
+    assert oracle.partial_blocks_if_tiled(g, 16)[0] == 0
+
+
+# ------------------------------------------------------------------ attention
+
+def _bruteforce_attention(q, k, v, F, T, wb, wa, r, scale):
+    """Token-by-token softmax with math.exp; the mask is written as frame
+    membership tests, independent of the oracle's vectorised rule."""
+    B, H, N, d = q.shape
+    out = np.zeros((B, H, N, d))
+    lse = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            for i in range(N):
+                fi = i // T
+                live = []
+                for j in range(N):
+                    fj = j // T
+                    if fj in range(fi - wb, fi + wa + 1) or fj == r:
+                        live.append(j)
+                logits = [scale * sum(q[b, h, i, t] * k[b, h, j, t] for t in range(d)) for j in live]
+                mx = max(logits)
+                w = [math.exp(x - mx) for x in logits]
+                tot = sum(w)
+                for t in range(d):
+                    out[b, h, i, t] = sum(wj * v[b, h, j, t] for wj, j in zip(w, live)) / tot
+                lse[b, h, i] = mx + math.log(tot)
+    return out, lse
+
+
+@pytest.mark.parametrize("geom", [(3, 4, 1, 1, 0), (4, 3, 0, 1, 2), (5, 2, 1, 0, -1), (2, 5, 0, 0, 1)])
+def test_attention_matches_bruteforce_loops(geom):
+    F, T, wb, wa, r = geom
+    rng = np.random.default_rng(F * 100 + T)
+    q, k, v = _rand_qkv(rng, 1, 2, F * T, 5)
+    g = oracle.MaskGeometry(F, T, wb, wa, r, 16, 16)     # blocks unused by attention_ref
+    o, lse = oracle.attention_ref(q, k, v, g, scale=0.7)
+    ob, lb = _bruteforce_attention(q, k, v, F, T, wb, wa, r, 0.7)
+    np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lb, rtol=0, atol=1e-12)
+
+
+def test_attention_dense_matches_torch_sdpa():
+    import torch
+    rng = np.random.default_rng(3)
+    F, T, d = 4, 24, 16
+    q, k, v = _rand_qkv(rng, 2, 3, F * T, d)
+    g = oracle.MaskGeometry(F, T, F, F, 0, 16, 16)       # window covers everything
+    o, _ = oracle.attention_ref(q, k, v, g)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v)).numpy()
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+
+
+def test_attention_windowed_matches_torch_sdpa_with_boolean_mask():
+    import torch
+    rng = np.random.default_rng(4)
+    F, T, d = 6, 16, 8
+    q, k, v = _rand_qkv(rng, 1, 2, F * T, d)
+    g = oracle.MaskGeometry(F, T, 1, 2, 5, 16, 16)
+    o, _ = oracle.attention_ref(q, k, v, g, scale=0.3)
+    fr = np.arange(F * T) // T
+    allowed = np.zeros((F * T, F * T), dtype=bool)
+    for i in range(F * T):
+        for j in range(F * T):
+            allowed[i, j] = (fr[i] - 1 <= fr[j] <= fr[i] + 2) or fr[j] == 5
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+        attn_mask=torch.from_numpy(allowed), scale=0.3).numpy()
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+
+
+def test_attention_closed_forms():
+    rng = np.random.default_rng(5)
+    F, T, d = 5, 16, 8
+    g = oracle.MaskGeometry(F, T, 1, 1, 0, 16, 16)
+    q, k, v = _rand_qkv(rng, 1, 2, F * T, d)
+    # Q = 0: every live key has weight 1/|live|, so O_i is the mean of V over row i's live keys
+    o, lse = oracle.attention_ref(np.zeros_like(q), k, v, g)
+    for i in range(F * T):
+        live = [j for j in range(F * T) if j // T in oracle.live_frames(g, i // T)]
+        np.testing.assert_allclose(o[:, :, i], v[:, :, live].mean(axis=2), atol=1e-12)
+        np.testing.assert_allclose(lse[:, :, i], math.log(len(live)), atol=1e-12)
+    # V rows all equal to c: O = c
+    c = rng.standard_normal(d)
+    o, _ = oracle.attention_ref(q, k, np.broadcast_to(c, v.shape), g)
+    np.testing.assert_allclose(o, np.broadcast_to(c, o.shape), atol=1e-12)
+    # common key offset k_j + c adds q_i . c to every logit of row i: O unchanged
+    o0, lse0 = oracle.attention_ref(q, k, v, g)
+    o1, lse1 = oracle.attention_ref(q, k + 3.0 * c, v, g)
+    np.testing.assert_allclose(o1, o0, atol=1e-11)
+    np.testing.assert_allclose(lse1 - lse0, 3.0 * (q @ c) / math.sqrt(d), atol=1e-10)
+    # permuting tokens inside each frame permutes the output rows the same way
+    perm = np.concatenate([f * T + rng.permutation(T) for f in range(F)])
+    o2, _ = oracle.attention_ref(q[:, :, perm], k[:, :, perm], v[:, :, perm], g)
+    np.testing.assert_allclose(o2, o0[:, :, perm], atol=1e-12)
+    # scaling q by a with scale 1/a is the same softmax
+    o3, _ = oracle.attention_ref(2.0 * q, k, v, g, scale=0.5 / math.sqrt(d))
+    np.testing.assert_allclose(o3, o0, atol=1e-12)
+
+
+def test_attention_rows_subset_matches_full():
+    rng = np.random.default_rng(6)
+    g = oracle.MaskGeometry(4, 32, 1, 1, 0, 16, 16)
+    q, k, v = _rand_qkv(rng, 1, 2, 128, 8)
+    o, lse = oracle.attention_ref(q, k, v, g)
+    rows = [0, 5, 31, 32, 77, 127]
+    os_, ls_ = oracle.attention_ref(q, k, v, g, rows=rows)
+    np.testing.assert_array_equal(os_, o[:, :, rows])
+    np.testing.assert_array_equal(ls_, lse[:, :, rows])
+
+
+def test_shift_invariance_online_fixed_and_max():
+    rng = np.random.default_rng(8)
+    g = oracle.MaskGeometry(5, 16, 1, 1, 0, 16, 16)
+    q, k, v = _rand_qkv(rng, 1, 2, 80, 8, kscale=2.0)
+    k = k + 5.0                                       # large common key component
+    o_ref, _ = oracle.attention_ref(q, k, v, g)
+    o_on = oracle.attention_online_ref(q, k, v, g, key_block=16)
+    np.testing.assert_allclose(o_on, o_ref, rtol=1e-12, atol=1e-13)
+    rec = oracle.head_bounds_ref(q, k, g)
+    for per_row in (False, True):
+        sh = oracle.row_shift_ref(q, rec, per_row=per_row)
+        o_fx = oracle.attention_fixed_shift_ref(q, k, v, g, sh)
+        np.testing.assert_allclose(o_fx, o_ref, rtol=1e-12, atol=1e-13)
+    # an arbitrary (even wrong-side) shift is still exact in fp64 while nothing under/overflows
+    o_any = oracle.attention_fixed_shift_ref(q, k, v, g, rng.standard_normal((1, 2, 80)) * 3)
+    np.testing.assert_allclose(o_any, o_ref, rtol=1e-12, atol=1e-13)
+
+
+def test_mean_centring_leaves_output_unchanged():
+    rng = np.random.default_rng(9)
+    g = oracle.MaskGeometry(4, 16, 1, 1, 0, 16, 16)
+    q, k, v = _rand_qkv(rng, 1, 1, 64, 8)
+    k = k + rng.standard_normal(8) * 4
+    rec = oracle.head_bounds_ref(q, k, g)
+    o0, _ = oracle.attention_ref(q, k, v, g)
+    o1, _ = oracle.attention_ref(q, k - rec["mu"][:, :, None, :], v, g)
+    np.testing.assert_allclose(o1, o0, atol=1e-12)
+
+
+# ------------------------------------------------------------------ bounds
+
+def test_bounds_hand_example():
+    # d = 2, one frame of 16 keys: 8 x (13, 14) and 8 x (7, 6); mean (10, 10),
+    # every centred key is +-(3, 4) with norm 5. One query (6, 8) of norm 10,
+    # the others zero. scale 1/sqrt(2): bound = 50/sqrt(2); single frame => c_max = 0.
+    k = np.zeros((1, 1, 16, 2)); k[0, 0, :8] = (13, 14); k[0, 0, 8:] = (7, 6)
+    q = np.zeros((1, 1, 16, 2)); q[0, 0, 3] = (6, 8)
+    g = oracle.MaskGeometry(1, 16, 0, 0, -1, 16, 16)
+    rec = oracle.head_bounds_ref(q, k, g)
+    np.testing.assert_allclose(rec["mu"][0, 0], [10, 10])
+    assert rec["q_max"][0, 0] == pytest.approx(10)
+    assert rec["k_max"][0, 0] == pytest.approx(5)
+    assert rec["bound"][0, 0] == pytest.approx(50 / math.sqrt(2))
+    assert rec["c_max"][0, 0] == pytest.approx(0, abs=1e-12)
+    # the bound is attained: q = (6,8) is parallel to the centred key (3,4)
+    s = oracle.live_logit_stats(q, k, g, rec["mu"])
+    assert s.max() == pytest.approx(50 / math.sqrt(2))
+
+
+def test_bounds_two_frame_window_mean_hand_example():
+    # 2 frames x 16 keys in d = 1, no reference frame, window 0 (block diagonal):
+    # frame 0 keys all +1, frame 1 keys all -3; mu = -1; every centred key has norm 2;
+    # each frame's live set is itself: window means +1 and -3, |mean - mu| = 2 for both.
+    k = np.zeros((1, 1, 32, 1)); k[0, 0, :16] = 1.0; k[0, 0, 16:] = -3.0
+    q = np.full((1, 1, 32, 1), 0.5)
+    g = oracle.MaskGeometry(2, 16, 0, 0, -1, 16, 16)
+    rec = oracle.head_bounds_ref(q, k, g, scale=1.0)
+    assert rec["mu"][0, 0, 0] == pytest.approx(-1)
+    assert rec["k_max"][0, 0] == pytest.approx(2)
+    assert rec["c_max"][0, 0] == pytest.approx(2)
+    assert rec["bound"][0, 0] == pytest.approx(1.0)
+    assert rec["gap_est"][0, 0] == pytest.approx(2.0)
+    # with the window covering both frames, the live mean is the global mean: c_max = 0
+    g2 = oracle.MaskGeometry(2, 16, 1, 1, -1, 16, 16)
+    assert oracle.head_bounds_ref(q, k, g2, scale=1.0)["c_max"][0, 0] == pytest.approx(0, abs=1e-12)
+
+
+def test_bounds_degenerate_cases():
+    rng = np.random.default_rng(10)
+    g = oracle.MaskGeometry(3, 16, 1, 1, 0, 16, 16)
+    q = rng.standard_normal((1, 2, 48, 8))
+    k = np.broadcast_to(rng.standard_normal(8), (1, 2, 48, 8)).copy()      # all keys equal
+    rec = oracle.head_bounds_ref(q, k, g)
+    np.testing.assert_allclose(rec["k_max"], 0, atol=1e-12)
+    np.testing.assert_allclose(rec["bound"], 0, atol=1e-12)
+    np.testing.assert_allclose(rec["c_max"], 0, atol=1e-12)
+    assert rec["eligible"].all()
+    rec0 = oracle.head_bounds_ref(np.zeros_like(q), rng.standard_normal((1, 2, 48, 8)), g)
+    np.testing.assert_allclose(rec0["bound"], 0)
+    np.testing.assert_allclose(rec0["gap_est"], 0)
+
+
+def test_bounds_translation_invariance():
+    rng = np.random.default_rng(11)
+    g = oracle.MaskGeometry(4, 16, 1, 1, 0, 16, 16)
+    q, k, _ = _rand_qkv(rng, 1, 2, 64, 8)
+    c = rng.standard_normal(8) * 10
+    r0 = oracle.head_bounds_ref(q, k, g)
+    r1 = oracle.head_bounds_ref(q, k + c, g)
+    np.testing.assert_allclose(r1["mu"], r0["mu"] + c, atol=1e-12)
+    for key in ("k_max", "c_max", "bound", "gap_est"):
+        np.testing.assert_allclose(r1[key], r0[key], rtol=1e-11)
+
+
+def _check_bound_audit(q, k, g, rows=None):
+    rec = oracle.head_bounds_ref(q, k, g)
+    stats = oracle.live_logit_stats(q, k, g, rec["mu"], rows=rows)     # (B, H, R) centred row maxima
+    bound = rec["bound"][:, :, None]
+    assert np.all(bound >= stats - 1e-12 * np.abs(stats))              # bound >= every live logit
+    row_gaps = bound - stats
+    assert np.all(rec["gap_est"][:, :, None] >= row_gaps - 1e-9)      # gap_est >= every row gap
+    head_gap = rec["bound"] - stats.max(axis=2)
+    assert np.all(rec["gap_est"] >= head_gap - 1e-9)
+    return rec, stats
+
+
+def test_bound_audit_exhaustive_small():
+    rng = np.random.default_rng(12)
+    for geom in [(5, 16, 1, 1, 0), (6, 16, 2, 0, 3), (4, 32, 0, 0, -1), (7, 16, 1, 1, 0)]:
+        F, T, wb, wa, r = geom
+        q, k, _ = _rand_qkv(rng, 2, 2, F * T, 8)
+        k = k + rng.standard_normal(8) * 3
+        _check_bound_audit(q, k, oracle.MaskGeometry(F, T, wb, wa, r, 16, 16))
+
+
+def test_bound_audit_workload1_exhaustive(config_inputs):
+    q, k, _ = config_inputs(1)
+    rec, stats = _check_bound_audit(q, k, _geom(workloads.config(1).mask_tuple()))
+    assert rec["eligible"].all()
+
+
+@pytest.mark.parametrize("i", [2, 3, 5])
+def test_bound_audit_workloads_sampled_rows_and_eligibility(config_inputs, i):
+    q, k, _ = config_inputs(i)
+    w = workloads.config(i)
+    g = _geom(w.mask_tuple())
+    rows = np.random.default_rng(i).choice(g.N, 24, replace=False)
+    rec, _ = _check_bound_audit(q, k, g, rows=rows)
+    assert rec["eligible"].all()
+    assert np.all(rec["gap_est"] < 25.0)
+
+
+def test_workload3_needs_mean_centring(config_inputs):
+    """Keys carry a per-head mean offset; the raw (uncentred) bound is above 30
+    nats while the centred one qualifies - the reason centring is done."""
+    q, k, _ = config_inputs(3)
+    g = _geom(workloads.config(3).mask_tuple())
+    rec = oracle.head_bounds_ref(q, k, g)
+    scale = 1 / math.sqrt(128)
+    raw_kmax = np.sqrt((np.asarray(k, np.float64) ** 2).sum(-1)).max(-1)
+    raw_bound = scale * rec["q_max"] * raw_kmax
+    assert np.all(raw_bound > 30.0)
+    assert rec["eligible"].all()
+
+
+def test_workload4_stressed_heads_fail_eligibility(config_inputs):
+    q, k, _ = config_inputs(4)
+    g = _geom(workloads.config(4).mask_tuple())
+    rec = oracle.head_bounds_ref(q, k, g)
+    elig = rec["eligible"][0]
+    assert [h for h in range(16) if not elig[h]] == list(workloads.STRESSED_HEADS)
+    assert np.all(rec["gap_est"][0, list(workloads.STRESSED_HEADS)] > 100.0)
+    # for such a head fp32 exp of (logit - shift) underflows to zero for whole rows
+    assert np.float32(np.exp(np.float32(-104.0))) == 0.0
+    rows = np.arange(0, g.N, 997)
+    stats = oracle.live_logit_stats(q[:, 5:6], k[:, 5:6], g, rec["mu"][:, 5:6], rows=rows)
+    gaps = rec["bound"][0, 5] - stats[0, 0]
+    assert np.any(gaps > 104.0)
+
+
+def test_live_flops_closed_form():
+    assert oracle.live_flops(_geom(workloads.config(2).mask_tuple()), 1, 8, 128) == 4 * 128 * 8 * 117 * 960 * 960
+    assert oracle.live_flops(_geom(workloads.config(5).mask_tuple()), 1, 4, 128) == 2727346176000
+
+
+# ------------------------------------------------------------------ planted mistakes
+
+def _run_pins_quietly(fns):
+    failed = 0
+    for fn in fns:
+        try:
+            fn()
+        except AssertionError:
+            failed += 1
+    return failed
+
+
+def test_planted_mistake_dropped_reference_frame_is_caught(monkeypatch):
+    def no_ref_rows(g, rows):
+        fr = np.arange(g.N) // g.T
+        fi = (np.asarray(rows) // g.T)[:, None]
+        return (fr[None, :] >= fi - g.wb) & (fr[None, :] <= fi + g.wa)
+    monkeypatch.setattr(O, "mask_rows", no_ref_rows)
+    assert _run_pins_quietly([test_plan_matches_hand_derived_golden,
+                              lambda: test_attention_matches_bruteforce_loops((3, 4, 1, 1, 0))]) == 2
+
+
+def test_planted_mistake_exclusive_window_is_caught(monkeypatch):
+    def excl_rows(g, rows):
+        fr = np.arange(g.N) // g.T
+        fi = (np.asarray(rows) // g.T)[:, None]
+        m = (fr[None, :] > fi - g.wb) & (fr[None, :] < fi + g.wa)
+        if g.r >= 0:
+            m |= fr[None, :] == g.r
+        return m
+    monkeypatch.setattr(O, "mask_rows", excl_rows)
+    assert _run_pins_quietly([test_plan_matches_hand_derived_golden,
+                              lambda: test_attention_matches_bruteforce_loops((3, 4, 1, 1, 0))]) == 2
+
+
+def test_planted_mistake_uncentred_bound_is_caught(monkeypatch):
+    real = O.head_bounds_ref
+
+    def uncentred(q, k, g, scale=None, threshold=30.0):
+        rec = real(q, k, g, scale, threshold)
+        d = np.asarray(q).shape[-1]
+        s = 1 / math.sqrt(d) if scale is None else scale
+        rec["k_max"] = np.sqrt((np.asarray(k, np.float64) ** 2).sum(-1)).max(-1)
+        rec["bound"] = s * rec["q_max"] * rec["k_max"]
+        return rec
+    monkeypatch.setattr(oracle, "head_bounds_ref", uncentred)
+    assert _run_pins_quietly([test_bounds_hand_example, test_bounds_translation_invariance]) == 2
+
+
+def test_planted_mistake_transposed_operand_is_caught(monkeypatch):
+    real = O.attention_ref
+
+    def swapped(q, k, v, g, scale=None, rows=None, chunk=256):
+        return real(q, v, k, g, scale, rows, chunk)            # K and V exchanged
+    monkeypatch.setattr(oracle, "attention_ref", swapped)
+    assert _run_pins_quietly([lambda: test_attention_matches_bruteforce_loops((3, 4, 1, 1, 0)),
+                              test_attention_dense_matches_torch_sdpa]) == 2
+
+
+def test_planted_mistake_missing_scale_is_caught(monkeypatch):
+    real = O.attention_ref
+
+    def unscaled(q, k, v, g, scale=None, rows=None, chunk=256):
+        return real(q, k, v, g, 1.0, rows, chunk)
+    monkeypatch.setattr(oracle, "attention_ref", unscaled)
+    assert _run_pins_quietly([lambda: test_attention_matches_bruteforce_loops((3, 4, 1, 1, 0)),
+                              test_attention_dense_matches_torch_sdpa]) == 2
