@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of the frame-structured block-sparse attention path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  plan (host, C ABI) -> copy to device -> head bounds (GPU) -> forward (GPU).
+Inputs are resident in HBM before timing starts. The metric counts live-block
+FLOPs only: 4 * d per live (query, key) pair (QK^T and PV), summed over
+every head.
+
+Prints ONE JSON line. The roofline object describes the dominant kernel
+(the forward) from HIP events recorded around each of its launches on the
+stream it runs on; `traffic` comes from the rocprofv3 counter summary in
+profiles/ when that summary was taken on the current kernel source.
+The CPU baseline times the fp64 oracle on a bounded row sample on the
+host cores (rank 0, N = 1 only).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "live-block attention TFLOP/s and % of bf16 MFMA peak, 1×MI355X"
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
+PEAK_HBM_GBS = 8000.0
+FWD_SOURCES = ["frame_block_sparse_amd/csrc/forward_bf16.hip", "frame_block_sparse_amd/csrc/forward_common.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in FWD_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per forward launch from profiles/forward_traffic_<workload>.txt
+    (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), or None if
+    absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"forward_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.lstrip().startswith("#"):
+            a, b = line.split(":", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, q, k, v, budget_s: float):
+    """fp64 oracle on a bounded sample of query rows (every frame, every
+    head), timed on the host cores. Rate in live TFLOP/s."""
+    import numpy as np
+    import oracle
+    g = oracle.MaskGeometry(*w.mask_tuple())
+    live_keys_per_row = {f: len(oracle.live_frames(g, f)) * g.T for f in range(g.F)}
+    rng = np.random.default_rng(123)
+
+    def sample(per_frame):
+        rows = []
+        for f in range(g.F):
+            rows += list(f * g.T + rng.choice(g.T, min(per_frame, g.T), replace=False))
+        return np.array(sorted(rows))
+
+    def timed(rows):
+        t0 = time.perf_counter()
+        oracle.attention_ref(q, k, v, g, rows=rows)
+        return time.perf_counter() - t0
+
+    rows = sample(2)
+    t = timed(rows)
+    per_frame = max(2, min(g.T, int(2 * budget_s / max(t, 1e-3))))
+    rows = sample(per_frame)
+    t = timed(rows)
+    flops = sum(4 * w.head_dim * live_keys_per_row[int(r) // g.T] for r in rows) * w.batch * w.heads
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(rows)} of {g.N} query rows ({per_frame} per frame), all {w.batch * w.heads} "
+                      f"(batch, head) pairs, fp64 dense-masked numpy, {t:.1f} s wall",
+            "seconds": round(t, 2), "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, help="1..5 (default 2: bf16, 21 frames x 960 tokens)")
+    ap.add_argument("--waves", type=int, default=0)
+    ap.add_argument("--rows", type=int, default=0)
+    ap.add_argument("--kstep", type=int, default=0)
+    ap.add_argument("--mode", default="auto", choices=["auto", "online", "fixed"])
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only (the path shards by heads with no "
+              "exchange inside it; multi-GPU runs are not part of it). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import ctypes
+    import frame_block_sparse_amd as fs
+    from frame_block_sparse_amd import fsattn as F
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    fs.lib()
+    w = workloads.config(args.workload)
+    print(f"[bench] workload {args.workload} {w.name}: generating inputs", file=sys.stderr, flush=True)
+    q, k, v = workloads.make_inputs(w, seed=0)
+    td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    qd, kd, vd = (torch.from_numpy(x).to(td).to(dev) for x in (q, k, v))
+    od = torch.empty_like(qd)
+    mask = F.to_mask(w)
+    nqb, nnz = fs.plan_size(mask)
+    flags = fs.make_flags(args.mode, waves=args.waves, rows_per_wave=args.rows, key_step=args.kstep)
+    waves, rows_pw, kstep, wgs, lds = fs.launch_info(tuple(qd.shape), fs.BF16 if w.dtype == "bf16" else fs.F32,
+                                                     mask, flags)
+    live_flops = 4.0 * w.head_dim * w.batch * w.heads * nnz * w.block_q * w.block_k
+    L = fs.lib()
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    # two pinned host plan buffers, alternated so the host never rewrites one a copy still reads
+    pins = [(torch.empty(nqb + 1, dtype=torch.int32).pin_memory(), torch.empty(nnz, dtype=torch.int32).pin_memory())
+            for _ in range(2)]
+    copied = [torch.cuda.Event(), torch.cuda.Event()]
+    for e in copied:
+        e.record()
+    rp_dev = torch.empty(nqb + 1, dtype=torch.int32, device=dev)
+    ci_dev = torch.empty(nnz, dtype=torch.int32, device=dev)
+    dplan = fs.DevicePlan(mask, rp_dev, ci_dev)
+    ws = torch.empty(max(1, fs.head_bounds_workspace_bytes(qd, mask)), dtype=torch.uint8, device=dev)
+    bnd = fs.Bounds(torch.empty((w.batch, w.heads, w.head_dim), dtype=torch.float32, device=dev),
+                    torch.empty((w.batch, w.heads, 8), dtype=torch.float32, device=dev))
+    total = args.warmup + args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(total)]
+
+    def step(i):
+        slot = i & 1
+        copied[slot].synchronize()
+        rp_h, ci_h = pins[slot]
+        st = L.fsattn_plan(ctypes.byref(mask), ctypes.cast(rp_h.data_ptr(), i32p), nqb + 1,
+                           ctypes.cast(ci_h.data_ptr(), i32p), nnz)
+        if st:
+            raise fs.FsattnError(st, "fsattn_plan")
+        rp_dev.copy_(rp_h, non_blocking=True)
+        ci_dev.copy_(ci_h, non_blocking=True)
+        copied[slot].record()
+        e0, e1, e2 = ev[i]
+        e0.record()
+        fs.head_bounds(qd, kd, mask, workspace=ws, out=bnd)
+        e1.record()
+        fs.forward(qd, kd, vd, dplan, bnd, flags=flags, out=od)
+        e2.record()
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(args.warmup, total):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+    fwd_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.warmup, total)]
+    bnd_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.warmup, total)]
+    fwd_avg = sum(fwd_ms) / len(fwd_ms)
+    bnd_avg = sum(bnd_ms) / len(bnd_ms)
+    achieved = live_flops / (fwd_avg * 1e-3) / 1e12
+    value = live_flops / (ms_step * 1e-3) / 1e12
+    elig = bnd.host()["eligible"]
+    esz = 2 if w.dtype == "bf16" else 4
+    bounds_bytes = 2.0 * w.batch * w.heads * w.seq_len * w.head_dim * esz
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {
+            "workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
+            "head_dim": w.head_dim, "frames": w.num_frames, "tokens_per_frame": w.tokens_per_frame,
+            "window": [w.window_before, w.window_after], "ref_frame": w.ref_frame,
+            "block_q": w.block_q, "block_k": w.block_k, "live_gflop": round(live_flops / 1e9, 3),
+            "mode": args.mode, "eligible_heads": int(elig.sum()),
+            "launch": {"waves": waves, "rows_per_wave": rows_pw, "key_step": kstep, "workgroups": wgs,
+                       "lds_bytes": lds},
+        },
+        "roofline": {
+            "kernel": "fwd_bf16_kernel" if w.dtype == "bf16" else "fwd_f32_kernel",
+            "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": read_traffic(w.name),
+            "avg_launch_ms": round(fwd_avg, 5), "algorithmic_flop_per_launch": live_flops,
+        },
+        "bounds": {"avg_ms": round(bnd_avg, 5), "algorithmic_bytes": bounds_bytes,
+                   "GBps": round(bounds_bytes / (bnd_avg * 1e-3) / 1e9, 1), "peak_GBps": PEAK_HBM_GBS},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle, bounded sample)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_baseline_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

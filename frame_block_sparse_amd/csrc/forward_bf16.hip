@@ -1,0 +1,420 @@
+// bf16 forward on MFMA: frame-block-sparse attention for gfx950.
+//
+// "HeyGen x Google Cloud: Bringing Avatar IV to TPUs":
+//  * "Deleting the Mask": blocks that divide the frame span are full or
+//    empty, so the inner loop is a dense attention loop over the live key
+//    ranges of the plan (window and reference frame in one pass), with no
+//    mask predicate, no padding and no second pass.
+//  * "Unchaining the Softmax", Fig. 4: on eligible heads every row starts
+//    with a precomputed shift derived from the small per-head record
+//    (Cauchy-Schwarz bound of the mean-centred logits plus scale*q_i.mu), so
+//    the inner loop has no running max and no rescaling; other heads take
+//    the online path (running max, rescale) inside the same kernel.
+//  * "Proving the Pixels Didn't Change": the final product PV runs in bf16 on
+//    the matrix unit (P rounded to bf16), accumulating in fp32.
+//
+// Work decomposition. A workgroup of W waves owns R = W * 16 * M16 query
+// rows of one frame of one (batch, head); all its rows share the frame's
+// key list, so each K/V step is staged once in LDS and reused by every
+// wave. A wave owns 16 * M16 rows. Per step of up to NK keys:
+//   S^T = K Q^T      v_mfma_f32_16x16x32_bf16, A = K rows from LDS, B = Q
+//                    held in registers; lane (g = lane/16, n = lane%16)
+//                    ends with S[q = n][keys 4g..4g+3] of each 16-key tile
+//   softmax          fp32 exp2 on those registers; the row statistics of
+//                    query n live in the four lanes n, n+16, n+32, n+48
+//   O^T += V^T P^T   the same MFMA with A = V^T read by ds_read_b64_tr_b16
+//                    (4 keys x 1 column per lane, hardware transpose) and
+//                    B = P^T, which is exactly the lane's own S registers
+//                    converted to bf16; a 16-key tail uses the 16x16x16 MFMA
+// so P never leaves registers and O's rows sit in the same lanes as S's.
+// K/V for the next step are loaded to registers while the current step is
+// computed, then written to the other LDS buffer (one barrier per step).
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+#include "forward_common.h"
+
+namespace fsattn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4;
+
+__device__ inline f4 mfma32(bf16x8 a, bf16x8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline f4 mfma16(bf16x4 a, bf16x4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+// Transposed LDS read: the 16 lanes of a group address a 4 x 16 block
+// (row j/4, columns 4*(j%4)..+3 for lane j); lane i receives column i of
+// the four rows.
+__device__ inline bf16x4 lds_read_tr(const __bf16 *p) {
+  const short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_short4 *)((__attribute__((address_space(3))) char *)p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+template <int M16, int W, int NK16, int D>
+__global__ __launch_bounds__(W * 64) void fwd_bf16_kernel(FwdParams p) {
+  constexpr int NT = W * 64;
+  constexpr int NK = NK16 * 16;
+  constexpr int KD = D / 32;         // 32-wide slices of d for QK^T
+  constexpr int DT = D / 16;         // 16-wide output column tiles for PV
+  constexpr int KP = D + 8;          // K row pitch in LDS (bank spread for 16-byte reads)
+  constexpr int VP = D + 16;         // V row pitch in LDS (bank spread for transposed reads)
+  constexpr int UPR = D / 8;         // 16-byte units per row
+  constexpr int UNITS = NK * UPR;    // per tensor per step
+  constexpr int UPT = (2 * UNITS + NT - 1) / NT;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  __bf16 *ksm = reinterpret_cast<__bf16 *>(smem);
+  __bf16 *vsm = ksm + 2 * NK * KP;
+  int2 *runs = reinterpret_cast<int2 *>(vsm + 2 * NK * VP);
+  int *nruns_sm = reinterpret_cast<int *>(runs + kMaxRuns);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, n16 = lane & 15;
+  const int tile = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / p.H, h = bh % p.H;
+  const int f = tile / p.tiles_per_frame, ti = tile % p.tiles_per_frame;
+  const int row0 = f * p.T + ti * p.rows_per_wg;
+  if (wave == 0) build_runs(p.row_ptr, p.col_idx, p.nnz, row0 / p.bq, p.bk, p.N, runs, nruns_sm);
+
+  const __bf16 *qb = static_cast<const __bf16 *>(p.q) + b * p.qsb + h * p.qsh;
+  const __bf16 *kb = static_cast<const __bf16 *>(p.k) + b * p.ksb + h * p.ksh;
+  const __bf16 *vb = static_cast<const __bf16 *>(p.v) + b * p.vsb + h * p.vsh;
+  const int wrow0 = row0 + wave * 16 * M16;
+
+  // Q fragments (B operand of S^T = K Q^T): row n16 of each 16-row group,
+  // d = 32*kd + 8*g .. +7.
+  bf16x8 qf[M16][KD];
+#pragma unroll
+  for (int m = 0; m < M16; ++m)
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd)
+      qf[m][kd] = *reinterpret_cast<const bf16x8 *>(qb + (int64_t)(wrow0 + 16 * m + n16) * p.qsn +
+                                                     32 * kd + 8 * g);
+
+  const int mode = p.flags & 3;
+  const bool fixed = mode == FSATTN_MODE_FORCE_FIXED ||
+                     (mode == FSATTN_MODE_AUTO && p.rec[bh].eligible != 0);
+  float sh[M16];   // fixed: the row's shift; online: the running max (log2 units)
+  if (fixed) {
+    const float *mu = p.key_mean + (int64_t)bh * D;
+    const float bound = p.rec[bh].bound, kmax = p.rec[bh].k_norm_max;
+    const bool per_row = (p.flags & FSATTN_SHIFT_PER_ROW) != 0;
+#pragma unroll
+    for (int m = 0; m < M16; ++m) {
+      float dot = 0.f, nq = 0.f;
+#pragma unroll
+      for (int kd = 0; kd < KD; ++kd)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float x = (float)qf[m][kd][t];
+          dot = fmaf(x, mu[32 * kd + 8 * g + t], dot);
+          nq = fmaf(x, x, nq);
+        }
+      dot += __shfl_xor(dot, 16);
+      dot += __shfl_xor(dot, 32);
+      nq += __shfl_xor(nq, 16);
+      nq += __shfl_xor(nq, 32);
+      const float mrow = per_row ? p.scale * (sqrtf(nq) * kmax + dot) : bound + p.scale * dot;
+      sh[m] = mrow * kLog2e;
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < M16; ++m) sh[m] = -INFINITY;
+  }
+  float lsum[M16];
+  f4 oacc[M16][DT];
+#pragma unroll
+  for (int m = 0; m < M16; ++m) {
+    lsum[m] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[m][dt] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float c2 = p.scale_log2;
+
+  __syncthreads();
+  const int nr = *nruns_sm;
+  int ri = 0, roff = 0;
+  auto next_step = [&](int &ks0, int &kl) -> bool {
+    while (ri < nr) {
+      const int s0 = runs[ri].x, s1 = runs[ri].y;
+      if (s0 + roff < s1) {
+        ks0 = s0 + roff;
+        kl = min(NK, s1 - ks0);
+        roff += kl;
+        return true;
+      }
+      ++ri;
+      roff = 0;
+    }
+    return false;
+  };
+
+  uint4 stg[UPT];
+  auto gload = [&](int ks0, int kl) {
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int idx = tid + u * NT;
+      if (idx < 2 * UNITS) {
+        const bool isv = idx >= UNITS;
+        const int li = isv ? idx - UNITS : idx;
+        const int r = li / UPR, c = li % UPR;
+        if (r < kl) {
+          const __bf16 *src = isv ? vb + (int64_t)(ks0 + r) * p.vsn : kb + (int64_t)(ks0 + r) * p.ksn;
+          stg[u] = *reinterpret_cast<const uint4 *>(src + c * 8);
+        }
+      }
+    }
+  };
+  auto lstore = [&](int buf, int kl) {
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int idx = tid + u * NT;
+      if (idx < 2 * UNITS) {
+        const bool isv = idx >= UNITS;
+        const int li = isv ? idx - UNITS : idx;
+        const int r = li / UPR, c = li % UPR;
+        if (r < kl) {
+          __bf16 *dst = isv ? vsm + buf * NK * VP + r * VP : ksm + buf * NK * KP + r * KP;
+          *reinterpret_cast<uint4 *>(dst + c * 8) = stg[u];
+        }
+      }
+    }
+  };
+
+  // One chunk of NS 16-key tiles (NS = 2, or 1 for a 16-key tail) starting
+  // at key row `key0` of the LDS buffers kt/vt.
+  auto chunk = [&](auto ns_tag, const __bf16 *kt, const __bf16 *vt, int key0) {
+    constexpr int NS = decltype(ns_tag)::value;
+    f4 s[M16][NS];
+#pragma unroll
+    for (int m = 0; m < M16; ++m)
+#pragma unroll
+      for (int t = 0; t < NS; ++t) s[m][t] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kd = 0; kd < KD; ++kd)
+#pragma unroll
+      for (int t = 0; t < NS; ++t) {
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8 *>(kt + (key0 + 16 * t + n16) * KP + 32 * kd + 8 * g);
+#pragma unroll
+        for (int m = 0; m < M16; ++m) s[m][t] = mfma32(a, qf[m][kd], s[m][t]);
+      }
+    if (!fixed) {
+      // Online softmax: raise the running max where a row's chunk maximum
+      // exceeds it; rescale only when some row of the wave changed.
+      float mn[M16];
+      bool raised = false;
+#pragma unroll
+      for (int m = 0; m < M16; ++m) {
+        float mx = s[m][0][0];
+#pragma unroll
+        for (int t = 0; t < NS; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[m][t][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mn[m] = fmaxf(sh[m], mx * c2);
+        raised |= mn[m] > sh[m];
+      }
+      if (__any(raised)) {
+#pragma unroll
+        for (int m = 0; m < M16; ++m) {
+          const float alpha = __builtin_amdgcn_exp2f(sh[m] - mn[m]);
+          sh[m] = mn[m];
+          lsum[m] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) oacc[m][dt] *= alpha;
+        }
+      }
+    }
+    bf16x8 pk[M16];
+    bf16x4 pt[M16];
+#pragma unroll
+    for (int m = 0; m < M16; ++m) {
+      const float nsh = -sh[m];
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(s[m][t][i], c2, nsh));
+          lsum[m] += e;
+          s[m][t][i] = e;
+        }
+      if constexpr (NS == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pk[m][i] = (__bf16)s[m][0][i];
+          pk[m][4 + i] = (__bf16)s[m][1][i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pt[m][i] = (__bf16)s[m][0][i];
+      }
+    }
+    const int vrow = key0 + 4 * g + (n16 >> 2), vcol = 4 * (n16 & 3);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      if constexpr (NS == 2) {
+        const bf16x4 lo = lds_read_tr(vt + vrow * VP + 16 * dt + vcol);
+        const bf16x4 hi = lds_read_tr(vt + (vrow + 16) * VP + 16 * dt + vcol);
+        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int m = 0; m < M16; ++m) oacc[m][dt] = mfma32(a, pk[m], oacc[m][dt]);
+      } else {
+        const bf16x4 a = lds_read_tr(vt + vrow * VP + 16 * dt + vcol);
+#pragma unroll
+        for (int m = 0; m < M16; ++m) oacc[m][dt] = mfma16(a, pt[m], oacc[m][dt]);
+      }
+    }
+  };
+  auto dispatch_step = [&](int kl, int buf) {
+    const __bf16 *kt = ksm + buf * NK * KP;
+    const __bf16 *vt = vsm + buf * NK * VP;
+    const int full = kl >> 5;
+    for (int c = 0; c < full; ++c) chunk(std::integral_constant<int, 2>{}, kt, vt, 32 * c);
+    if (kl & 16) chunk(std::integral_constant<int, 1>{}, kt, vt, kl - 16);
+  };
+
+  int cs0 = 0, ckl = 0;
+  bool have = next_step(cs0, ckl);
+  if (have) {
+    gload(cs0, ckl);
+    lstore(0, ckl);
+  }
+  __syncthreads();
+  int buf = 0;
+  while (have) {
+    int ns0 = 0, nkl = 0;
+    const bool more = next_step(ns0, nkl);
+    if (more) gload(ns0, nkl);
+    dispatch_step(ckl, buf);
+    if (more) lstore(buf ^ 1, nkl);
+    __syncthreads();
+    buf ^= 1;
+    have = more;
+    cs0 = ns0;
+    ckl = nkl;
+  }
+
+  // Epilogue: one cross-lane reduction of the row sums, normalise, store.
+#pragma unroll
+  for (int m = 0; m < M16; ++m) {
+    float l = lsum[m];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const float inv = 1.f / l;
+    const int row = wrow0 + 16 * m + n16;
+    if (p.o_f32) {
+      float *orow = static_cast<float *>(p.o) + b * p.osb + h * p.osh + (int64_t)row * p.osn;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const f4 x = oacc[m][dt] * inv;
+        *reinterpret_cast<float4 *>(orow + 16 * dt + 4 * g) = make_float4(x[0], x[1], x[2], x[3]);
+      }
+    } else {
+      __bf16 *orow = static_cast<__bf16 *>(p.o) + b * p.osb + h * p.osh + (int64_t)row * p.osn;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const f4 x = oacc[m][dt] * inv;
+        bf16x4 y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = (__bf16)x[i];
+        *reinterpret_cast<bf16x4 *>(orow + 16 * dt + 4 * g) = y;
+      }
+    }
+    if (p.lse && g == 0) p.lse[(int64_t)bh * p.N + row] = (sh[m] + log2f(l)) * kLn2;
+  }
+}
+
+template <int M16, int W, int NK16, int D>
+hipError_t launch_one(const FwdParams &p, const FwdConfig &c, hipStream_t st) {
+  auto kern = fwd_bf16_kernel<M16, W, NK16, D>;
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [&] {
+    attr_err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  });
+  if (attr_err != hipSuccess) return attr_err;
+  hipLaunchKernelGGL(kern, dim3(p.F * p.tiles_per_frame, p.B * p.H), dim3(W * 64), c.lds_bytes, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// (rows per wave / 16, waves per workgroup) pairs built, in order of
+// preference; the first whose workgroup tile divides the frame span wins.
+static const int kShapes[][2] = {{4, 4}, {5, 4}, {4, 3}, {5, 3}, {3, 5}, {3, 4}, {5, 2},
+                                 {4, 2}, {3, 3}, {3, 2}, {2, 4}, {2, 2}, {1, 1}};
+
+int fwd_bf16_lds_bytes(int nk16, int D) {
+  const int NK = nk16 * 16;
+  return 2 * NK * (D + 8) * 2 + 2 * NK * (D + 16) * 2 + kMaxRuns * 8 + 16;
+}
+
+bool choose_fwd_config(const fsattn_shape *s, const fsattn_mask *m, uint32_t flags, FwdConfig *cfg) {
+  const int T = m->tokens_per_frame;
+  const int BH = s->batch * s->heads;
+  if (s->dtype == FSATTN_F32) {
+    const int R = f32_rows_per_wg(T);
+    cfg->waves = 1;
+    cfg->m16 = R / 16;
+    cfg->nk16 = 1;
+    cfg->lds_bytes = 2 * 16 * s->head_dim * 4 + kMaxRuns * 8 + 4;
+    cfg->grid = (int64_t)m->num_frames * (T / R) * BH;
+    return true;
+  }
+  const int wo = (flags >> 8) & 15, mo = (flags >> 12) & 15, so = (flags >> 16) & 15;
+  const int nk16 = so ? so : 4;
+  if (nk16 != 2 && nk16 != 4) return false;
+  for (const auto &sh : kShapes) {
+    const int m16 = sh[0], w = sh[1];
+    if ((wo && w != wo) || (mo && m16 != mo)) continue;
+    const int R = 16 * m16 * w;
+    if (T % R) continue;
+    cfg->waves = w;
+    cfg->m16 = m16;
+    cfg->nk16 = nk16;
+    cfg->lds_bytes = fwd_bf16_lds_bytes(nk16, s->head_dim);
+    cfg->grid = (int64_t)m->num_frames * (T / R) * BH;
+    return true;
+  }
+  return false;
+}
+
+#define FSATTN_SHAPE_CASE(M, W)                                               \
+  if (c.m16 == M && c.waves == W) {                                           \
+    if (head_dim == 128)                                                      \
+      return c.nk16 == 4 ? launch_one<M, W, 4, 128>(p, c, st)                 \
+                         : launch_one<M, W, 2, 128>(p, c, st);                \
+    return c.nk16 == 4 ? launch_one<M, W, 4, 64>(p, c, st)                    \
+                       : launch_one<M, W, 2, 64>(p, c, st);                   \
+  }
+
+hipError_t launch_forward_bf16(const FwdParams &p, const FwdConfig &c, int head_dim, hipStream_t st) {
+  FSATTN_SHAPE_CASE(4, 4)
+  FSATTN_SHAPE_CASE(5, 4)
+  FSATTN_SHAPE_CASE(4, 3)
+  FSATTN_SHAPE_CASE(5, 3)
+  FSATTN_SHAPE_CASE(3, 5)
+  FSATTN_SHAPE_CASE(3, 4)
+  FSATTN_SHAPE_CASE(5, 2)
+  FSATTN_SHAPE_CASE(4, 2)
+  FSATTN_SHAPE_CASE(3, 3)
+  FSATTN_SHAPE_CASE(3, 2)
+  FSATTN_SHAPE_CASE(2, 4)
+  FSATTN_SHAPE_CASE(2, 2)
+  FSATTN_SHAPE_CASE(1, 1)
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fsattn

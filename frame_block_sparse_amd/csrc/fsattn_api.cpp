@@ -1,0 +1,199 @@
+// C entry points: argument validation, workspace layout and dispatch.
+// Every check runs on the host before any launch; on error nothing is
+// launched and no output is written.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "fsattn.h"
+#include "fsattn_internal.h"
+
+using namespace fsattn;
+
+namespace {
+
+constexpr int kBoundsChunk = 128;   // tokens per bounds-kernel workgroup (within one frame)
+
+int elem_size(int dtype) { return dtype == FSATTN_BF16 ? 2 : 4; }
+
+fsattn_status check_shape(const fsattn_shape *s, const fsattn_mask *m) {
+  if (!s || !m) return FSATTN_ERR_INVALID_ARGUMENT;
+  if (!geometry_ok(m)) return FSATTN_ERR_BLOCK_GEOMETRY;
+  if (s->batch < 1 || s->heads < 1) return FSATTN_ERR_INVALID_ARGUMENT;
+  if ((int64_t)s->seq_len != (int64_t)m->num_frames * m->tokens_per_frame) return FSATTN_ERR_INVALID_ARGUMENT;
+  if (s->head_dim != 64 && s->head_dim != 128) return FSATTN_ERR_UNSUPPORTED;
+  if (s->dtype != FSATTN_F32 && s->dtype != FSATTN_BF16) return FSATTN_ERR_UNSUPPORTED;
+  if ((int64_t)s->batch * s->heads > 65535) return FSATTN_ERR_UNSUPPORTED;
+  return FSATTN_OK;
+}
+
+fsattn_status check_tensor(const fsattn_tensor &t, int esz, int head_dim) {
+  if (!t.data) return FSATTN_ERR_INVALID_ARGUMENT;
+  if (reinterpret_cast<uintptr_t>(t.data) % 16) return FSATTN_ERR_INVALID_ARGUMENT;
+  if (t.stride_b < 0 || t.stride_h < 0 || t.stride_n < head_dim) return FSATTN_ERR_INVALID_ARGUMENT;
+  if ((t.stride_b * esz) % 16 || (t.stride_h * esz) % 16 || (t.stride_n * esz) % 16)
+    return FSATTN_ERR_INVALID_ARGUMENT;
+  return FSATTN_OK;
+}
+
+struct WsLayout {
+  size_t part, frame, qmax, kmax, q2, total;
+  int chunks_per_frame;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+WsLayout ws_layout(const fsattn_shape *s, const fsattn_mask *m) {
+  WsLayout w;
+  const int64_t BH = (int64_t)s->batch * s->heads;
+  w.chunks_per_frame = (m->tokens_per_frame + kBoundsChunk - 1) / kBoundsChunk;
+  const int64_t NC = (int64_t)m->num_frames * w.chunks_per_frame;
+  const int64_t D = s->head_dim;
+  size_t off = 0;
+  w.part = off;  off = align256(off + sizeof(float) * BH * NC * D);
+  w.frame = off; off = align256(off + sizeof(float) * BH * m->num_frames * D);
+  w.qmax = off;  off = align256(off + sizeof(float) * BH * NC);
+  w.kmax = off;  off = align256(off + sizeof(float) * BH * NC);
+  w.q2 = off;    off = align256(off + sizeof(float) * BH);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" int fsattn_abi_version(void) { return FSATTN_ABI_VERSION; }
+
+extern "C" const char *fsattn_status_string(fsattn_status st) {
+  switch (st) {
+    case FSATTN_OK: return "ok";
+    case FSATTN_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case FSATTN_ERR_BLOCK_GEOMETRY:
+      return "block sizes must be positive multiples of 16 dividing tokens_per_frame";
+    case FSATTN_ERR_UNSUPPORTED: return "unsupported head_dim, dtype or launch shape";
+    case FSATTN_ERR_BUFFER_TOO_SMALL: return "buffer too small";
+    case FSATTN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+extern "C" size_t fsattn_head_bounds_workspace_bytes(const fsattn_shape *s, const fsattn_mask *m) {
+  if (check_shape(s, m) != FSATTN_OK) return 0;
+  return ws_layout(s, m).total;
+}
+
+extern "C" fsattn_status fsattn_head_bounds(void *hip_stream, const fsattn_shape *s, const fsattn_mask *m,
+                                            fsattn_tensor q, fsattn_tensor k, float scale,
+                                            float gap_threshold_nats, float *key_mean,
+                                            fsattn_head_bound *rec, void *workspace,
+                                            size_t workspace_bytes) {
+  fsattn_status st = check_shape(s, m);
+  if (st != FSATTN_OK) return st;
+  const int esz = elem_size(s->dtype);
+  if ((st = check_tensor(q, esz, s->head_dim)) != FSATTN_OK) return st;
+  if ((st = check_tensor(k, esz, s->head_dim)) != FSATTN_OK) return st;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return FSATTN_ERR_INVALID_ARGUMENT;
+  if (!(gap_threshold_nats >= 0.f)) return FSATTN_ERR_INVALID_ARGUMENT;
+  if (!key_mean || !rec || !workspace) return FSATTN_ERR_INVALID_ARGUMENT;
+  const WsLayout w = ws_layout(s, m);
+  if (workspace_bytes < w.total) return FSATTN_ERR_BUFFER_TOO_SMALL;
+  BoundsParams p;
+  p.q = q.data; p.k = k.data;
+  p.qsb = q.stride_b; p.qsh = q.stride_h; p.qsn = q.stride_n;
+  p.ksb = k.stride_b; p.ksh = k.stride_h; p.ksn = k.stride_n;
+  p.B = s->batch; p.H = s->heads; p.N = s->seq_len; p.F = m->num_frames; p.T = m->tokens_per_frame;
+  p.D = s->head_dim;
+  p.wr = m->window_before; p.wa = m->window_after; p.ref = m->ref_frame;
+  p.chunk = kBoundsChunk; p.chunks_per_frame = w.chunks_per_frame;
+  p.scale = scale; p.threshold = gap_threshold_nats;
+  p.key_mean = key_mean; p.rec = rec;
+  char *base = static_cast<char *>(workspace);
+  p.ws_part = reinterpret_cast<float *>(base + w.part);
+  p.ws_frame = reinterpret_cast<float *>(base + w.frame);
+  p.ws_qmax = reinterpret_cast<float *>(base + w.qmax);
+  p.ws_kmax = reinterpret_cast<float *>(base + w.kmax);
+  p.ws_q2 = reinterpret_cast<float *>(base + w.q2);
+  const hipError_t e = launch_head_bounds(p, s->dtype, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? FSATTN_OK : FSATTN_ERR_HIP;
+}
+
+namespace {
+
+constexpr uint32_t kKnownFlags = 0x7u | (0xfu << 8) | (0xfu << 12) | (0xfu << 16);
+
+fsattn_status check_forward_host(const fsattn_shape *s, const fsattn_mask *m, uint32_t flags, FwdConfig *cfg) {
+  fsattn_status st = check_shape(s, m);
+  if (st != FSATTN_OK) return st;
+  if (flags & ~kKnownFlags) return FSATTN_ERR_INVALID_ARGUMENT;
+  if ((flags & 3) == 3) return FSATTN_ERR_INVALID_ARGUMENT;
+  if (max_runs_per_frame(m) > kMaxRuns) return FSATTN_ERR_UNSUPPORTED;
+  if (s->dtype == FSATTN_F32 && (flags & (0xfffu << 8))) return FSATTN_ERR_UNSUPPORTED;
+  if (!choose_fwd_config(s, m, flags, cfg)) return FSATTN_ERR_UNSUPPORTED;
+  if (cfg->grid / ((int64_t)s->batch * s->heads) > INT32_MAX) return FSATTN_ERR_UNSUPPORTED;
+  return FSATTN_OK;
+}
+
+}  // namespace
+
+extern "C" fsattn_status fsattn_forward_launch_info(const fsattn_shape *s, const fsattn_mask *m, uint32_t flags,
+                                                    int32_t *waves, int32_t *rows_per_wave, int32_t *key_step,
+                                                    int64_t *workgroups, int32_t *lds_bytes) {
+  FwdConfig c;
+  const fsattn_status st = check_forward_host(s, m, flags, &c);
+  if (st != FSATTN_OK) return st;
+  if (waves) *waves = c.waves;
+  if (rows_per_wave) *rows_per_wave = 16 * c.m16;
+  if (key_step) *key_step = 16 * c.nk16;
+  if (workgroups) *workgroups = c.grid;
+  if (lds_bytes) *lds_bytes = c.lds_bytes;
+  return FSATTN_OK;
+}
+
+extern "C" fsattn_status fsattn_forward(void *hip_stream, const fsattn_shape *s, const fsattn_mask *m,
+                                        const int32_t *row_ptr, const int32_t *col_idx, int64_t nnz,
+                                        fsattn_tensor q, fsattn_tensor k, fsattn_tensor v, fsattn_tensor o,
+                                        int32_t o_dtype, const float *key_mean, const fsattn_head_bound *rec,
+                                        float scale, uint32_t flags, float *lse) {
+  FwdConfig cfg;
+  fsattn_status st = check_forward_host(s, m, flags, &cfg);
+  if (st != FSATTN_OK) return st;
+  const int esz = elem_size(s->dtype);
+  if ((st = check_tensor(q, esz, s->head_dim)) != FSATTN_OK) return st;
+  if ((st = check_tensor(k, esz, s->head_dim)) != FSATTN_OK) return st;
+  if ((st = check_tensor(v, esz, s->head_dim)) != FSATTN_OK) return st;
+  if (o_dtype != s->dtype && o_dtype != FSATTN_F32) return FSATTN_ERR_UNSUPPORTED;
+  if ((st = check_tensor(o, elem_size(o_dtype), s->head_dim)) != FSATTN_OK) return st;
+  if (!row_ptr || !col_idx) return FSATTN_ERR_INVALID_ARGUMENT;
+  int64_t nqb = 0, want_nnz = 0;
+  if ((st = fsattn_plan_size(m, &nqb, &want_nnz)) != FSATTN_OK) return st;
+  if (nnz != want_nnz) return FSATTN_ERR_INVALID_ARGUMENT;
+  const int mode = flags & 3;
+  if (mode != FSATTN_MODE_FORCE_ONLINE && (!key_mean || !rec)) return FSATTN_ERR_INVALID_ARGUMENT;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return FSATTN_ERR_INVALID_ARGUMENT;
+
+  FwdParams p;
+  p.q = q.data; p.k = k.data; p.v = v.data; p.o = o.data;
+  p.qsb = q.stride_b; p.qsh = q.stride_h; p.qsn = q.stride_n;
+  p.ksb = k.stride_b; p.ksh = k.stride_h; p.ksn = k.stride_n;
+  p.vsb = v.stride_b; p.vsh = v.stride_h; p.vsn = v.stride_n;
+  p.osb = o.stride_b; p.osh = o.stride_h; p.osn = o.stride_n;
+  p.row_ptr = row_ptr; p.col_idx = col_idx; p.nnz = nnz;
+  p.key_mean = key_mean; p.rec = rec; p.lse = lse;
+  p.B = s->batch; p.H = s->heads; p.N = s->seq_len; p.F = m->num_frames; p.T = m->tokens_per_frame;
+  p.bq = m->block_q; p.bk = m->block_k;
+  p.scale = scale; p.scale_log2 = scale * kLog2e;
+  p.flags = flags;
+  p.o_f32 = o_dtype == FSATTN_F32 ? 1 : 0;
+  const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  hipError_t e;
+  if (s->dtype == FSATTN_F32) {
+    p.rows_per_wg = f32_rows_per_wg(p.T);
+    p.tiles_per_frame = p.T / p.rows_per_wg;
+    e = launch_forward_f32(p, s->head_dim, stream);
+  } else {
+    p.rows_per_wg = 16 * cfg.m16 * cfg.waves;
+    p.tiles_per_frame = p.T / p.rows_per_wg;
+    e = launch_forward_bf16(p, cfg, s->head_dim, stream);
+  }
+  return e == hipSuccess ? FSATTN_OK : FSATTN_ERR_HIP;
+}

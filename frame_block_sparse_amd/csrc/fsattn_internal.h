@@ -1,0 +1,67 @@
+// Internal declarations shared by the host layer and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include "fsattn.h"
+
+namespace fsattn {
+
+constexpr int kMaxRuns = 64;        // contiguous key runs per query frame kept in LDS
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Host-side geometry helpers (fsattn_plan.cpp).
+bool geometry_ok(const fsattn_mask *m);
+// Live frames of query frame f in ascending order; returns the count.
+int live_frames(const fsattn_mask *m, int f, int *out, int cap);
+int64_t live_frame_count(const fsattn_mask *m, int f);
+// Largest number of contiguous key-frame runs over all query frames.
+int max_runs_per_frame(const fsattn_mask *m);
+
+struct BoundsParams {
+  const void *q, *k;
+  int64_t qsb, qsh, qsn, ksb, ksh, ksn;
+  int B, H, N, F, T, D;
+  int wr, wa, ref;              // window and reference frame
+  int chunk, chunks_per_frame;  // token chunk (within one frame)
+  float scale, threshold;
+  float *key_mean;
+  fsattn_head_bound *rec;
+  float *ws_part;     // [BH][NC][D] partial key sums
+  float *ws_frame;    // [BH][F][D]  per-frame key sums
+  float *ws_qmax;     // [BH][NC]    partial max |q|^2
+  float *ws_kmax;     // [BH][NC]    partial max |k - mu|^2
+  float *ws_q2;       // [BH]        max |q|^2
+};
+
+hipError_t launch_head_bounds(const BoundsParams &p, int dtype, hipStream_t st);
+
+struct FwdParams {
+  const void *q, *k, *v;
+  void *o;
+  int64_t qsb, qsh, qsn, ksb, ksh, ksn, vsb, vsh, vsn, osb, osh, osn;
+  const int32_t *row_ptr, *col_idx;
+  int64_t nnz;
+  const float *key_mean;
+  const fsattn_head_bound *rec;
+  float *lse;
+  int B, H, N, F, T, bq, bk;
+  int rows_per_wg, tiles_per_frame;
+  float scale, scale_log2;
+  uint32_t flags;
+  int o_f32;
+};
+
+struct FwdConfig {
+  int waves, m16, nk16;   // waves per workgroup, rows per wave / 16, keys per step / 16
+  int lds_bytes;
+  int64_t grid;
+};
+
+// Chooses (or validates an override of) the launch shape; false if none fits.
+bool choose_fwd_config(const fsattn_shape *s, const fsattn_mask *m, uint32_t flags, FwdConfig *cfg);
+hipError_t launch_forward_bf16(const FwdParams &p, const FwdConfig &c, int head_dim, hipStream_t st);
+hipError_t launch_forward_f32(const FwdParams &p, int head_dim, hipStream_t st);
+int f32_rows_per_wg(int T);
+
+}  // namespace fsattn

@@ -1,0 +1,281 @@
+"""ctypes binding of libfsattn.so.
+
+Argument marshalling only: every step of the attention path runs in the HIP
+library. PyTorch provides device memory and the current stream. If the
+library is not built, every call raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfsattn.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fsattn.h")
+
+F32, BF16 = 0, 1
+MODE_AUTO, MODE_FORCE_ONLINE, MODE_FORCE_FIXED, SHIFT_PER_ROW = 0, 1, 2, 4
+DEFAULT_GAP_NATS = 30.0
+
+STATUS_NAMES = {0: "FSATTN_OK", 1: "FSATTN_ERR_INVALID_ARGUMENT", 2: "FSATTN_ERR_BLOCK_GEOMETRY",
+                3: "FSATTN_ERR_UNSUPPORTED", 4: "FSATTN_ERR_BUFFER_TOO_SMALL", 5: "FSATTN_ERR_HIP"}
+
+
+class Mask(ctypes.Structure):
+    _fields_ = [("num_frames", ctypes.c_int32), ("tokens_per_frame", ctypes.c_int32),
+                ("window_before", ctypes.c_int32), ("window_after", ctypes.c_int32),
+                ("ref_frame", ctypes.c_int32), ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32)]
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class Tensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64)]
+
+
+class HeadBound(ctypes.Structure):
+    _fields_ = [("q_norm_max", ctypes.c_float), ("k_norm_max", ctypes.c_float), ("c_max", ctypes.c_float),
+                ("bound", ctypes.c_float), ("gap_est", ctypes.c_float), ("eligible", ctypes.c_int32),
+                ("pad", ctypes.c_int32 * 2)]
+
+
+class FsattnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS_NAMES.get(status, status)} ({status_string(status)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run `python -m frame_block_sparse_amd._build` "
+                           "(or __graft_entry__.build()); there is no CPU fallback")
+    L = ctypes.CDLL(LIB_PATH)
+    c_i32p = ctypes.POINTER(ctypes.c_int32)
+    c_i64p = ctypes.POINTER(ctypes.c_int64)
+    L.fsattn_plan_size.argtypes = [ctypes.POINTER(Mask), c_i64p, c_i64p]
+    L.fsattn_plan.argtypes = [ctypes.POINTER(Mask), c_i32p, ctypes.c_int64, c_i32p, ctypes.c_int64]
+    L.fsattn_head_bounds_workspace_bytes.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Mask)]
+    L.fsattn_head_bounds_workspace_bytes.restype = ctypes.c_size_t
+    L.fsattn_head_bounds.argtypes = [ctypes.c_void_p, ctypes.POINTER(Shape), ctypes.POINTER(Mask), Tensor, Tensor,
+                                     ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_size_t]
+    L.fsattn_forward.argtypes = [ctypes.c_void_p, ctypes.POINTER(Shape), ctypes.POINTER(Mask),
+                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                 Tensor, Tensor, Tensor, Tensor, ctypes.c_int32, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_float, ctypes.c_uint32, ctypes.c_void_p]
+    L.fsattn_forward_launch_info.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Mask), ctypes.c_uint32,
+                                             c_i32p, c_i32p, c_i32p, c_i64p, c_i32p]
+    L.fsattn_status_string.argtypes = [ctypes.c_int]
+    L.fsattn_status_string.restype = ctypes.c_char_p
+    L.fsattn_abi_version.argtypes = []
+    for name in ("fsattn_plan_size", "fsattn_plan", "fsattn_head_bounds", "fsattn_forward",
+                 "fsattn_forward_launch_info"):
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_string(st: int) -> str:
+    return lib().fsattn_status_string(st).decode()
+
+
+def abi_version() -> int:
+    return lib().fsattn_abi_version()
+
+
+def declared_functions():
+    """Names of the functions include/fsattn.h declares."""
+    text = open(HEADER_PATH).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w ]+?\*?\s*(fsattn_\w+)\s*\(", text, re.M)))
+
+
+def _check(st: int, what: str):
+    if st != 0:
+        raise FsattnError(st, what)
+
+
+def to_mask(mask) -> Mask:
+    """A Mask from a Mask, a 7-tuple (num_frames, tokens_per_frame,
+    window_before, window_after, ref_frame, block_q, block_k) or any object
+    with a mask_tuple() method."""
+    if isinstance(mask, Mask):
+        return mask
+    if hasattr(mask, "mask_tuple"):
+        mask = mask.mask_tuple()
+    return Mask(*[int(x) for x in mask])
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise FsattnError(3, f"unsupported tensor dtype {t.dtype}")
+
+
+def _tensor(t: torch.Tensor) -> Tensor:
+    if t.dim() != 4:
+        raise FsattnError(1, "tensors must be [B, H, N, d]")
+    if t.stride(3) != 1:
+        raise FsattnError(1, "the head dimension must be contiguous")
+    sb, sh, sn, _ = t.stride()
+    return Tensor(t.data_ptr(), sb, sh, sn)
+
+
+def _shape(q: torch.Tensor) -> Shape:
+    B, H, N, d = q.shape
+    return Shape(B, H, N, d, _dtype_code(q))
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+# ----------------------------------------------------------------- plan
+
+def plan_size(mask) -> Tuple[int, int]:
+    m = to_mask(mask)
+    nqb, nnz = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().fsattn_plan_size(ctypes.byref(m), ctypes.byref(nqb), ctypes.byref(nnz)), "fsattn_plan_size")
+    return nqb.value, nnz.value
+
+
+def plan(mask) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(row_ptr, col_idx) as CPU int32 tensors."""
+    m = to_mask(mask)
+    nqb, nnz = plan_size(m)
+    rp = torch.empty(nqb + 1, dtype=torch.int32)
+    ci = torch.empty(max(nnz, 1), dtype=torch.int32)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    _check(lib().fsattn_plan(ctypes.byref(m), ctypes.cast(rp.data_ptr(), i32p), rp.numel(),
+                             ctypes.cast(ci.data_ptr(), i32p), ci.numel()), "fsattn_plan")
+    return rp, ci[:nnz]
+
+
+@dataclass
+class DevicePlan:
+    mask: Mask
+    row_ptr: torch.Tensor
+    col_idx: torch.Tensor
+
+    @property
+    def nnz(self) -> int:
+        return self.col_idx.numel()
+
+
+def device_plan(mask, device) -> DevicePlan:
+    m = to_mask(mask)
+    rp, ci = plan(m)
+    if ci.numel() == 0:
+        ci = torch.zeros(1, dtype=torch.int32)[:0]
+    return DevicePlan(m, rp.to(device), ci.to(device))
+
+
+# ----------------------------------------------------------------- bounds
+
+@dataclass
+class Bounds:
+    key_mean: torch.Tensor      # [B, H, d] fp32 (device)
+    rec: torch.Tensor           # [B, H, 8] fp32 raw records (device)
+
+    def host(self):
+        """The records decoded on the host: dict of [B, H] numpy arrays."""
+        r = self.rec.detach().cpu()
+        return dict(q_norm_max=r[..., 0].numpy(), k_norm_max=r[..., 1].numpy(), c_max=r[..., 2].numpy(),
+                    bound=r[..., 3].numpy(), gap_est=r[..., 4].numpy(),
+                    eligible=r[..., 5].contiguous().view(torch.int32).numpy())
+
+
+def head_bounds_workspace_bytes(q: torch.Tensor, mask) -> int:
+    m = to_mask(mask)
+    s = _shape(q)
+    return lib().fsattn_head_bounds_workspace_bytes(ctypes.byref(s), ctypes.byref(m))
+
+
+def head_bounds(q: torch.Tensor, k: torch.Tensor, mask, scale: Optional[float] = None,
+                threshold: float = DEFAULT_GAP_NATS, workspace: Optional[torch.Tensor] = None,
+                out: Optional[Bounds] = None) -> Bounds:
+    m = to_mask(mask)
+    s = _shape(q)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    L = lib()
+    need = L.fsattn_head_bounds_workspace_bytes(ctypes.byref(s), ctypes.byref(m))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = Bounds(torch.empty((B, H, d), dtype=torch.float32, device=q.device),
+                     torch.empty((B, H, 8), dtype=torch.float32, device=q.device))
+    _check(L.fsattn_head_bounds(_stream(q), ctypes.byref(s), ctypes.byref(m), _tensor(q), _tensor(k),
+                                float(scale), float(threshold), out.key_mean.data_ptr(), out.rec.data_ptr(),
+                                workspace.data_ptr(), workspace.numel()), "fsattn_head_bounds")
+    return out
+
+
+# ----------------------------------------------------------------- forward
+
+_MODES = {"auto": MODE_AUTO, "online": MODE_FORCE_ONLINE, "fixed": MODE_FORCE_FIXED}
+
+
+def make_flags(mode: str = "auto", per_row_shift: bool = False, waves: int = 0, rows_per_wave: int = 0,
+               key_step: int = 0) -> int:
+    f = _MODES[mode]
+    if per_row_shift:
+        f |= SHIFT_PER_ROW
+    f |= (waves & 15) << 8
+    f |= ((rows_per_wave // 16) & 15) << 12
+    f |= ((key_step // 16) & 15) << 16
+    return f
+
+
+def launch_info(q_shape, dtype: int, mask, flags: int = 0):
+    """(waves, rows_per_wave, key_step, workgroups, lds_bytes) of a forward."""
+    B, H, N, d = q_shape
+    s = Shape(B, H, N, d, dtype)
+    m = to_mask(mask)
+    w, r, k, l = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    g = ctypes.c_int64()
+    _check(lib().fsattn_forward_launch_info(ctypes.byref(s), ctypes.byref(m), flags, ctypes.byref(w),
+                                            ctypes.byref(r), ctypes.byref(k), ctypes.byref(g), ctypes.byref(l)),
+           "fsattn_forward_launch_info")
+    return w.value, r.value, k.value, g.value, l.value
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dplan: DevicePlan,
+            bounds: Optional[Bounds], scale: Optional[float] = None, flags: int = 0,
+            out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+            lse: Optional[torch.Tensor] = None, stream: Optional[int] = None) -> torch.Tensor:
+    """Attention over the plan's live blocks. Returns `out` ([B, H, N, d])."""
+    s = _shape(q)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype or q.dtype, device=q.device)
+    o_code = _dtype_code(out)
+    km = bounds.key_mean.data_ptr() if bounds is not None else None
+    rc = bounds.rec.data_ptr() if bounds is not None else None
+    _check(lib().fsattn_forward(stream if stream is not None else _stream(q), ctypes.byref(s),
+                                ctypes.byref(dplan.mask), dplan.row_ptr.data_ptr(), dplan.col_idx.data_ptr(),
+                                dplan.nnz, _tensor(q), _tensor(k), _tensor(v), _tensor(out), o_code,
+                                km, rc, float(scale), int(flags),
+                                lse.data_ptr() if lse is not None else None), "fsattn_forward")
+    return out

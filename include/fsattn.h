@@ -1,0 +1,224 @@
+/*
+ * fsattn - frame-structured block-sparse attention for AMD MI355X (gfx950).
+ *
+ * C ABI of the library libfsattn.so. Three calls make the hot path:
+ *   fsattn_plan         live key blocks per query block (host, bit-exact)
+ *   fsattn_head_bounds  key mean, norm maxima, logit bound, eligibility (GPU)
+ *   fsattn_forward      attention over the live blocks, fixed-shift or
+ *                       online softmax chosen per head (GPU)
+ *
+ * The method is the one described in "HeyGen x Google Cloud: Bringing
+ * Avatar IV to TPUs" (Google Developers Blog). Section names below refer to
+ * the headings of that post.
+ *
+ * Conventions shared by every call:
+ *  - Ownership: the caller owns every buffer, host or device. The library
+ *    never allocates device memory, never synchronises a stream and keeps
+ *    no mutable global state.
+ *  - Errors: arguments are validated on the host before any launch. On any
+ *    error nothing is launched and no output is written. A failed launch is
+ *    reported as FSATTN_ERR_HIP. Device faults surface on the stream.
+ *  - Streams: `hip_stream` is a hipStream_t passed as void*; NULL means the
+ *    null stream. GPU calls are asynchronous on that stream.
+ *  - Layout ("Layout Is the ABI": the producer's layout is consumed as is,
+ *    no repack): every tensor is [B, H, N, d] with arbitrary element strides
+ *    for B, H and N and unit stride along d. Data pointers and the N stride
+ *    in bytes must be multiples of 16.
+ *  - Tokens are frame-major: token t belongs to frame t / tokens_per_frame.
+ */
+#ifndef FSATTN_H
+#define FSATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FSATTN_ABI_VERSION 1
+
+typedef enum fsattn_status {
+  FSATTN_OK = 0,
+  FSATTN_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad stride, size mismatch */
+  FSATTN_ERR_BLOCK_GEOMETRY = 2,   /* blocks not multiples of 16 dividing the frame span */
+  FSATTN_ERR_UNSUPPORTED = 3,      /* head_dim / dtype combination not built */
+  FSATTN_ERR_BUFFER_TOO_SMALL = 4, /* caller buffer shorter than required */
+  FSATTN_ERR_HIP = 5               /* a HIP runtime call or launch failed */
+} fsattn_status;
+
+/* Element types. */
+enum { FSATTN_F32 = 0, FSATTN_BF16 = 1 };
+
+/*
+ * The frame-structured mask and its block tiling ("Deleting the Mask",
+ * Fig. 3). Query frame f sees the key frames of the window
+ * [f - window_before, f + window_after] clamped to [0, num_frames - 1],
+ * plus frame ref_frame (-1: no reference frame). block_q and block_k must
+ * be positive multiples of 16 that divide tokens_per_frame, so that every
+ * block is entirely live or entirely masked.
+ */
+typedef struct fsattn_mask {
+  int32_t num_frames;
+  int32_t tokens_per_frame;
+  int32_t window_before;
+  int32_t window_after;
+  int32_t ref_frame;
+  int32_t block_q;
+  int32_t block_k;
+} fsattn_mask;
+
+/* Problem shape. seq_len must equal num_frames * tokens_per_frame.
+ * head_dim is 64 or 128. dtype is FSATTN_F32 or FSATTN_BF16 and applies to
+ * Q, K and V alike. */
+typedef struct fsattn_shape {
+  int32_t batch;
+  int32_t heads;
+  int32_t seq_len;
+  int32_t head_dim;
+  int32_t dtype;
+} fsattn_shape;
+
+/* A strided [B, H, N, d] device tensor. Strides are in elements. */
+typedef struct fsattn_tensor {
+  void *data;
+  int64_t stride_b;
+  int64_t stride_h;
+  int64_t stride_n;
+} fsattn_tensor;
+
+/*
+ * Per-(batch, head) record written by fsattn_head_bounds ("Unchaining the
+ * Softmax": the small array of precomputed norms the kernel reads as each
+ * row starts). All values use the softmax scale passed to the call.
+ *   q_norm_max = max_i |q_i|
+ *   k_norm_max = max_j |k_j - mu|            (mu = key mean of the head)
+ *   c_max      = max_f |kbar_f - mu|         (kbar_f = mean of the keys
+ *                                             live for query frame f)
+ *   bound      = scale * q_norm_max * k_norm_max
+ *                (Cauchy-Schwarz: >= scale * q_i . (k_j - mu) for all i, j)
+ *   gap_est    = scale * q_norm_max * (k_norm_max + c_max)
+ *                (>= bound minus the largest live logit of every row)
+ *   eligible   = gap_est <= gap_threshold_nats (1) or not (0)
+ * 32 bytes, naturally aligned.
+ */
+typedef struct fsattn_head_bound {
+  float q_norm_max;
+  float k_norm_max;
+  float c_max;
+  float bound;
+  float gap_est;
+  int32_t eligible;
+  int32_t pad[2];
+} fsattn_head_bound;
+
+/* fsattn_forward flags. */
+enum {
+  FSATTN_MODE_AUTO = 0,          /* fixed shift on eligible heads, online elsewhere */
+  FSATTN_MODE_FORCE_ONLINE = 1,  /* online softmax on every head */
+  FSATTN_MODE_FORCE_FIXED = 2,   /* fixed shift on every head (testing; an
+                                    ineligible head may underflow to 0/0) */
+  FSATTN_SHIFT_PER_ROW = 4       /* fixed shift scale*(|q_i|*k_norm_max + q_i.mu)
+                                    instead of bound + scale*q_i.mu */
+};
+/* Optional launch-shape overrides in the flags word (0 = library choice):
+ * bits 8..11 waves per workgroup (1..8), bits 12..15 query rows per wave
+ * divided by 16 (2..5), bits 16..19 keys per pipeline step divided by 16
+ * (2 or 4). An override that does not fit the geometry returns
+ * FSATTN_ERR_UNSUPPORTED. */
+#define FSATTN_FLAG_WAVES(n) ((uint32_t)(n) << 8)
+#define FSATTN_FLAG_ROWS16(m) ((uint32_t)(m) << 12)
+#define FSATTN_FLAG_KSTEP16(s) ((uint32_t)(s) << 16)
+
+#define FSATTN_DEFAULT_GAP_NATS 30.0f
+
+/*
+ * Plan size: number of query blocks (seq_len / block_q) and number of live
+ * (query block, key block) pairs, nnz = sum_f |L(f)| * (T/block_q) *
+ * (T/block_k). Host only. Errors: INVALID_ARGUMENT (null pointer),
+ * BLOCK_GEOMETRY.
+ */
+fsattn_status fsattn_plan_size(const fsattn_mask *m, int64_t *num_q_blocks, int64_t *nnz);
+
+/*
+ * The block plan ("Deleting the Mask": blocks that divide the frame span
+ * are full or empty, and the reference frame's blocks are just more full
+ * blocks of the same pass). Writes CSR arrays into caller-owned HOST
+ * memory: row_ptr[num_q_blocks + 1] with row_ptr[0] = 0, and col_idx[nnz]
+ * holding, for each query block in order, its live key blocks in
+ * ascending order. The plan depends on the mask only and is shared by
+ * every batch and head. Host only, deterministic, bit-exact.
+ * Errors: INVALID_ARGUMENT, BLOCK_GEOMETRY, BUFFER_TOO_SMALL.
+ */
+fsattn_status fsattn_plan(const fsattn_mask *m, int32_t *row_ptr, int64_t row_ptr_len,
+                          int32_t *col_idx, int64_t col_idx_len);
+
+/* Bytes of device workspace fsattn_head_bounds needs for this shape and
+ * mask; 0 if the arguments are invalid. */
+size_t fsattn_head_bounds_workspace_bytes(const fsattn_shape *s, const fsattn_mask *m);
+
+/*
+ * Per-head bounds and eligibility ("Unchaining the Softmax": mean-centred
+ * keys, norm maxima, Cauchy-Schwarz bound, per-head eligibility; the bound
+ * audit for windowed masks gives c_max). Reads Q and K (device), writes
+ * key_mean[B*H*head_dim] (fp32, device; the mean over all N keys of each
+ * head) and rec[B*H] (device), using the caller's device workspace
+ * (>= fsattn_head_bounds_workspace_bytes). Reductions run in a fixed order
+ * without atomics: results are bitwise reproducible. scale > 0;
+ * gap_threshold_nats >= 0. Asynchronous on hip_stream.
+ * Errors: INVALID_ARGUMENT, BLOCK_GEOMETRY, UNSUPPORTED,
+ * BUFFER_TOO_SMALL (workspace), HIP.
+ */
+fsattn_status fsattn_head_bounds(void *hip_stream, const fsattn_shape *s, const fsattn_mask *m,
+                                 fsattn_tensor q, fsattn_tensor k, float scale,
+                                 float gap_threshold_nats, float *key_mean,
+                                 fsattn_head_bound *rec, void *workspace, size_t workspace_bytes);
+
+/*
+ * Attention over the live blocks:
+ *   O_i = sum_{j live for i} exp(scale*q_i.k_j - m_i) v_j / sum_j exp(...)
+ * in one pass over the plan's key blocks ("Deleting the Mask"), with m_i
+ * either the precomputed per-row shift (fixed path, "Unchaining the
+ * Softmax", Fig. 4 lower) or the running max (online path, Fig. 4 upper),
+ * chosen per head from rec[].eligible and flags. QK^T and PV run on bf16
+ * MFMA with fp32 accumulation for bf16 inputs (P is rounded to bf16 for
+ * PV); fp32 inputs are computed in fp32 throughout.
+ *
+ * row_ptr/col_idx: DEVICE copies of fsattn_plan's output for the same mask
+ * (nnz entries); the kernel relies on all query blocks of a frame sharing
+ * one list, which fsattn_plan guarantees. key_mean/rec: fsattn_head_bounds'
+ * output for the same Q/K and scale (needed by the fixed path; may be NULL
+ * only with FSATTN_MODE_FORCE_ONLINE). o: output [B,H,N,d] of o_dtype
+ * (the input dtype, or FSATTN_F32). lse: optional device [B*H*N] fp32
+ * log-sum-exp (natural log) per row, or NULL. Asynchronous on hip_stream;
+ * deterministic (no atomics).
+ * Errors: INVALID_ARGUMENT (incl. nnz not matching the mask), BLOCK_GEOMETRY,
+ * UNSUPPORTED, HIP.
+ */
+fsattn_status fsattn_forward(void *hip_stream, const fsattn_shape *s, const fsattn_mask *m,
+                             const int32_t *row_ptr, const int32_t *col_idx, int64_t nnz,
+                             fsattn_tensor q, fsattn_tensor k, fsattn_tensor v, fsattn_tensor o,
+                             int32_t o_dtype, const float *key_mean, const fsattn_head_bound *rec,
+                             float scale, uint32_t flags, float *lse);
+
+/*
+ * Launch shape fsattn_forward would use for these arguments (host only):
+ * waves per workgroup, query rows per wave, keys per pipeline step,
+ * workgroups in the grid and dynamic LDS bytes per workgroup. Any output
+ * pointer may be NULL. Errors: as fsattn_forward's host validation.
+ */
+fsattn_status fsattn_forward_launch_info(const fsattn_shape *s, const fsattn_mask *m, uint32_t flags,
+                                         int32_t *waves, int32_t *rows_per_wave, int32_t *key_step,
+                                         int64_t *workgroups, int32_t *lds_bytes);
+
+/* Static description of a status code. */
+const char *fsattn_status_string(fsattn_status st);
+
+/* FSATTN_ABI_VERSION of the built library. */
+int fsattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FSATTN_H */

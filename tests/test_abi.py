@@ -1,0 +1,175 @@
+"""C-ABI tests that need no GPU: the library loads, exports every declared
+symbol, plans bit-exactly like the oracle, and rejects bad arguments on the
+host before any launch (no compute call is made here)."""
+import ctypes
+import subprocess
+
+import numpy as np
+import pytest
+
+import frame_block_sparse_amd as fs
+from frame_block_sparse_amd import fsattn as F
+import oracle
+import workloads
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = fs.lib()
+    names = F.declared_functions()
+    assert {"fsattn_plan", "fsattn_head_bounds", "fsattn_forward"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", F.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for n in names:
+        assert n in exported, n
+    assert fs.abi_version() == 1
+
+
+def test_struct_layouts():
+    assert ctypes.sizeof(F.Mask) == 28
+    assert ctypes.sizeof(F.Shape) == 20
+    assert ctypes.sizeof(F.Tensor) == 32
+    assert ctypes.sizeof(F.HeadBound) == 32
+
+
+@pytest.mark.parametrize("i", [1, 2, 3, 4, 5])
+def test_plan_bit_exact_vs_oracle_on_workloads(i):
+    w = workloads.config(i)
+    rp, ci = fs.plan(w)
+    orp, oci = oracle.plan_bruteforce(oracle.MaskGeometry(*w.mask_tuple()))
+    assert np.array_equal(rp.numpy(), orp)
+    assert np.array_equal(ci.numpy(), oci)
+    assert fs.plan_size(w) == (len(orp) - 1, len(oci))
+
+
+def test_plan_bit_exact_vs_oracle_random_geometries():
+    rng = np.random.default_rng(21)
+    for _ in range(60):
+        T = 16 * int(rng.integers(1, 9))
+        divs = [b for b in range(16, T + 1, 16) if T % b == 0]
+        Fn = int(rng.integers(1, 12))
+        t = (Fn, T, int(rng.integers(0, 5)), int(rng.integers(0, 5)), int(rng.integers(-1, Fn)),
+             int(rng.choice(divs)), int(rng.choice(divs)))
+        rp, ci = fs.plan(t)
+        orp, oci = oracle.plan_bruteforce(oracle.MaskGeometry(*t))
+        assert np.array_equal(rp.numpy(), orp), t
+        assert np.array_equal(ci.numpy(), oci), t
+
+
+def test_plan_golden():
+    import json, os
+    cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "plan_tiny.json")))["cases"]
+    for c in cases:
+        rp, ci = fs.plan(c["mask"])
+        assert rp.tolist() == c["row_ptr"] and ci.tolist() == c["col_idx"], c["name"]
+
+
+@pytest.mark.parametrize("mask,status", [
+    ((3, 48, 1, 1, 0, 32, 16), 2), ((3, 48, 1, 1, 0, 24, 16), 2), ((3, 48, 1, 1, 0, 16, 0), 2),
+    ((3, 48, -1, 1, 0, 16, 16), 2), ((3, 48, 1, 1, 3, 16, 16), 2), ((3, 48, 1, 1, -2, 16, 16), 2),
+    ((0, 48, 1, 1, -1, 16, 16), 2), ((3, 40, 1, 1, 0, 16, 16), 2)])
+def test_plan_rejects_bad_geometry(mask, status):
+    with pytest.raises(fs.FsattnError) as e:
+        fs.plan_size(mask)
+    assert e.value.status == status
+
+
+def test_plan_buffer_too_small_leaves_output_untouched():
+    m = F.to_mask((5, 48, 1, 1, 0, 16, 16))
+    rp = (ctypes.c_int32 * 16)(*([-7] * 16))
+    ci = (ctypes.c_int32 * 143)(*([-7] * 143))
+    st = fs.lib().fsattn_plan(ctypes.byref(m), rp, 16, ci, 143)
+    assert st == 4
+    assert list(rp) == [-7] * 16 and list(ci) == [-7] * 143
+    st = fs.lib().fsattn_plan(ctypes.byref(m), rp, 15, ci, 144 if False else 143)
+    assert st == 4
+
+
+# ---- argument validation of the GPU entry points (host-side, nothing launched)
+
+FAKE = 0x7f0000000000          # 16-byte aligned, never dereferenced: every call below fails validation
+
+
+def _t(ptr=FAKE, n=240, d=64, h=2):
+    return F.Tensor(ptr, h * n * d, n * d, d)
+
+
+def _bounds_call(shape=None, mask=None, q=None, k=None, scale=0.125, thr=30.0, km=FAKE, rec=FAKE, ws=FAKE,
+                 wsb=1 << 30):
+    s = shape or F.Shape(1, 2, 240, 64, 0)
+    m = mask or F.to_mask((5, 48, 1, 1, 0, 16, 16))
+    return fs.lib().fsattn_head_bounds(None, ctypes.byref(s), ctypes.byref(m), q or _t(), k or _t(),
+                                       scale, thr, km, rec, ws, wsb)
+
+
+def _fwd_call(shape=None, mask=None, nnz=144, q=None, k=None, v=None, o=None, odt=0, km=FAKE, rec=FAKE,
+              scale=0.125, flags=0, rp=FAKE, ci=FAKE):
+    s = shape or F.Shape(1, 2, 240, 64, 0)
+    m = mask or F.to_mask((5, 48, 1, 1, 0, 16, 16))
+    return fs.lib().fsattn_forward(None, ctypes.byref(s), ctypes.byref(m), rp, ci, nnz, q or _t(), k or _t(),
+                                   v or _t(), o or _t(), odt, km, rec, scale, flags, None)
+
+
+def test_head_bounds_validation():
+    assert _bounds_call(shape=F.Shape(1, 2, 241, 64, 0)) == 1                  # seq_len != F*T
+    assert _bounds_call(shape=F.Shape(1, 2, 240, 96, 0)) == 3                  # head_dim
+    assert _bounds_call(shape=F.Shape(1, 2, 240, 64, 7)) == 3                  # dtype
+    assert _bounds_call(shape=F.Shape(0, 2, 240, 64, 0)) == 1
+    assert _bounds_call(mask=F.to_mask((5, 48, 1, 1, 0, 32, 16))) == 2
+    assert _bounds_call(q=_t(FAKE + 4)) == 1                                    # misaligned
+    assert _bounds_call(k=F.Tensor(FAKE, 1, 1, 63)) == 1                       # rows overlap / stride
+    assert _bounds_call(k=F.Tensor(0, 1, 1, 64)) == 1                          # null
+    assert _bounds_call(scale=0.0) == 1
+    assert _bounds_call(scale=float("nan")) == 1
+    assert _bounds_call(thr=-1.0) == 1
+    assert _bounds_call(km=None) == 1
+    assert _bounds_call(rec=None) == 1
+    assert _bounds_call(ws=None) == 1
+    assert _bounds_call(wsb=16) == 4
+
+
+def test_workspace_bytes():
+    L = fs.lib()
+    s = F.Shape(1, 4, 48960, 128, 1)
+    m = F.to_mask(workloads.config(5))
+    assert L.fsattn_head_bounds_workspace_bytes(ctypes.byref(s), ctypes.byref(m)) > 4 * 128 * 6 * 4
+    bad = F.Shape(1, 4, 48961, 128, 1)
+    assert L.fsattn_head_bounds_workspace_bytes(ctypes.byref(bad), ctypes.byref(m)) == 0
+
+
+def test_forward_validation():
+    assert _fwd_call(nnz=143) == 1                                             # plan does not match mask
+    assert _fwd_call(shape=F.Shape(1, 2, 240, 128, 3)) == 3
+    assert _fwd_call(mask=F.to_mask((5, 48, 1, 1, 0, 48, 32))) == 2
+    assert _fwd_call(flags=3) == 1                                             # both modes
+    assert _fwd_call(flags=1 << 24) == 1                                       # unknown bit
+    assert _fwd_call(km=None) == 1                                             # fixed path needs the record
+    assert _fwd_call(rp=None) == 1
+    assert _fwd_call(ci=None) == 1
+    assert _fwd_call(o=_t(FAKE + 8)) == 1
+    assert _fwd_call(odt=1) == 3                                               # fp32 input, bf16 output
+    assert _fwd_call(scale=-1.0) == 1
+    assert _fwd_call(flags=fs.make_flags(waves=4)) == 3                        # fp32 path has no overrides
+
+
+def test_launch_info_choices():
+    for i in (2, 3, 4, 5):
+        w = workloads.config(i)
+        waves, rows, kstep, wgs, lds = fs.launch_info((w.batch, w.heads, w.seq_len, w.head_dim), fs.BF16, w)
+        assert w.tokens_per_frame % (waves * rows) == 0
+        assert wgs == w.batch * w.heads * w.seq_len // (waves * rows)
+        assert lds <= 160 * 1024
+    w = workloads.config(3)
+    with pytest.raises(fs.FsattnError) as e:      # 4 waves x 64 rows does not divide 3600
+        fs.launch_info((1, 5, 32400, 128), fs.BF16, w, fs.make_flags(waves=4, rows_per_wave=64))
+    assert e.value.status == 3
+    waves, rows, _, _, _ = fs.launch_info((1, 5, 32400, 128), fs.BF16, w, fs.make_flags(waves=5, rows_per_wave=48))
+    assert (waves, rows) == (5, 48)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(F, "_lib", None)
+    monkeypatch.setattr(F, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        F.lib()
