@@ -16,7 +16,7 @@
 // Work decomposition. A workgroup of W waves owns R = W * 16 * M16 query
 // rows of one frame of one (batch, head); all its rows share the frame's
 // key list, so each K/V step is staged once in LDS and reused by every
-// wave. A wave owns 16 * M16 rows. Per step of up to NK keys:
+// wave. A wave owns 16 * M16 rows. Per 32-key chunk of a step:
 //   S^T = K Q^T      v_mfma_f32_16x16x32_bf16, A = K rows from LDS, B = Q
 //                    held in registers; lane (g = lane/16, n = lane%16)
 //                    ends with S[q = n][keys 4g..4g+3] of each 16-key tile
@@ -27,8 +27,20 @@
 //                    B = P^T, which is exactly the lane's own S registers
 //                    converted to bf16; a 16-key tail uses the 16x16x16 MFMA
 // so P never leaves registers and O's rows sit in the same lanes as S's.
-// K/V for the next step are loaded to registers while the current step is
-// computed, then written to the other LDS buffer (one barrier per step).
+//
+// Staging. K/V steps go global -> LDS with global_load_lds_dwordx4 (no
+// registers in between): each wave instruction writes 1 KB of consecutive
+// LDS, so rows are unpadded and bank conflicts are removed by an XOR
+// swizzle of 16-byte chunks instead (K: chunk ^ (row & 7), which spreads
+// the 8 rows an MFMA operand read touches per cycle; V: chunk ^ 2*(row & 3),
+// which spreads the 4 rows of a transposed read). The next step is loaded
+// into the other buffer while the current one is computed; one barrier per
+// step.
+//
+// Order. Workgroups are issued heavy frames first (frames seeing the most
+// key frames), and the (frame, head) groups are dealt round-robin to the 8
+// XCDs so that all tiles of a group, which stream the same K/V, run on one
+// XCD and share its L2.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -43,6 +55,11 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) unsigned char lds_uchar;
+typedef __attribute__((address_space(1))) void glb_void;
+
+constexpr int kXcds = 8;
 
 __device__ inline f4 mfma32(bf16x8 a, bf16x8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -53,35 +70,80 @@ __device__ inline f4 mfma16(bf16x4 a, bf16x4 b, f4 c) {
 // Transposed LDS read: the 16 lanes of a group address a 4 x 16 block
 // (row j/4, columns 4*(j%4)..+3 for lane j); lane i receives column i of
 // the four rows.
-__device__ inline bf16x4 lds_read_tr(const __bf16 *p) {
-  const short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_short4 *)((__attribute__((address_space(3))) char *)p));
+__device__ inline bf16x4 lds_read_tr(const unsigned char *p) {
+  const short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)((lds_uchar *)p));
   return __builtin_bit_cast(bf16x4, r);
+}
+
+// One wave-wide global -> LDS copy of 16 bytes per lane
+// (global_load_lds_dwordx4): lane l's bytes land at LDS address lds + 16*l.
+// Issued from inline assembly so that the compiler's wait insertion, which
+// cannot tell the two staging buffers apart, does not stall every LDS read
+// behind the in-flight prefetch; completion is awaited explicitly
+// (wait_vmem() before the step barrier). M0 carries the LDS base; no
+// other code in these kernels uses M0.
+__device__ inline void dma16(const void *src, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
+}
+
+// s_waitcnt vmcnt(0) through the builtin, which the compiler's own wait
+// tracking sees (it does not parse inline assembly): after it, no vector
+// memory load is considered outstanding, so no wait for an earlier load is
+// sunk into the step loop, where it would also stall on the prefetch.
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// Workgroup index -> (frame, batch*head, tile within the frame).
+__device__ inline void map_block(const FwdParams &p, int bid, int &f, int &bh, int &tile) {
+  const int BH = p.B * p.H;
+  const int TPF = p.tiles_per_frame;
+  const int NG = p.F * BH;                 // (frame, head) groups
+  const int G = NG * TPF;
+  // the hardware dispatches workgroup ids round-robin over the XCDs; give
+  // each XCD a contiguous range of the logical order
+  const int xcd = bid % kXcds, local = bid / kXcds;
+  const int per = G / kXcds, rem = G % kXcds;
+  const int li = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+  // logical order: 8 piles, pile q holding groups q, q+8, ... (heavy first)
+  const int A = NG / kXcds, Rg = NG % kXcds;
+  const int big = (A + 1) * TPF;
+  int pile, off;
+  if (li < Rg * big) {
+    pile = li / big;
+    off = li % big;
+  } else {
+    const int l2 = li - Rg * big;
+    pile = Rg + l2 / (A * TPF);
+    off = l2 % (A * TPF);
+  }
+  const int gi = pile + kXcds * (off / TPF);
+  tile = off % TPF;
+  const int fr = gi / BH;
+  bh = gi % BH;
+  f = p.ordered ? p.frame_order[fr] : fr;
 }
 
 template <int M16, int W, int NK16, int D>
 __global__ __launch_bounds__(W * 64) void fwd_bf16_kernel(FwdParams p) {
-  constexpr int NT = W * 64;
   constexpr int NK = NK16 * 16;
-  constexpr int KD = D / 32;         // 32-wide slices of d for QK^T
-  constexpr int DT = D / 16;         // 16-wide output column tiles for PV
-  constexpr int KP = D + 8;          // K row pitch in LDS (bank spread for 16-byte reads)
-  constexpr int VP = D + 16;         // V row pitch in LDS (bank spread for transposed reads)
-  constexpr int UPR = D / 8;         // 16-byte units per row
-  constexpr int UNITS = NK * UPR;    // per tensor per step
-  constexpr int UPT = (2 * UNITS + NT - 1) / NT;
+  constexpr int KD = D / 32;          // 32-wide slices of d for QK^T
+  constexpr int DT = D / 16;          // 16-wide output column tiles for PV
+  constexpr int ROWB = 2 * D;         // bytes per K/V row in LDS
+  constexpr int TILEB = NK * ROWB;    // bytes of one K (or V) tile
+  constexpr int RPI = 1024 / ROWB;    // rows written by one wave-wide 16-byte load
+  constexpr int NI = NK / RPI;        // such loads per tile
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
 
   extern __shared__ __align__(16) unsigned char smem[];
-  __bf16 *ksm = reinterpret_cast<__bf16 *>(smem);
-  __bf16 *vsm = ksm + 2 * NK * KP;
-  int2 *runs = reinterpret_cast<int2 *>(vsm + 2 * NK * VP);
+  // [buf 0: K tile, V tile][buf 1: K tile, V tile], then the runs
+  int2 *runs = reinterpret_cast<int2 *>(smem + 4 * TILEB);
   int *nruns_sm = reinterpret_cast<int *>(runs + kMaxRuns);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, n16 = lane & 15;
-  const int tile = blockIdx.x, bh = blockIdx.y;
+  int f, bh, ti;
+  map_block(p, blockIdx.x, f, bh, ti);
   const int b = bh / p.H, h = bh % p.H;
-  const int f = tile / p.tiles_per_frame, ti = tile % p.tiles_per_frame;
   const int row0 = f * p.T + ti * p.rows_per_wg;
   if (wave == 0) build_runs(p.row_ptr, p.col_idx, p.nnz, row0 / p.bq, p.bk, p.N, runs, nruns_sm);
 
@@ -99,6 +161,7 @@ __global__ __launch_bounds__(W * 64) void fwd_bf16_kernel(FwdParams p) {
     for (int kd = 0; kd < KD; ++kd)
       qf[m][kd] = *reinterpret_cast<const bf16x8 *>(qb + (int64_t)(wrow0 + 16 * m + n16) * p.qsn +
                                                      32 * kd + 8 * g);
+  wait_vmem();
 
   const int mode = p.flags & 3;
   const bool fixed = mode == FSATTN_MODE_FORCE_FIXED ||
@@ -158,41 +221,28 @@ __global__ __launch_bounds__(W * 64) void fwd_bf16_kernel(FwdParams p) {
     return false;
   };
 
-  uint4 stg[UPT];
-  auto gload = [&](int ks0, int kl) {
-#pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int idx = tid + u * NT;
-      if (idx < 2 * UNITS) {
-        const bool isv = idx >= UNITS;
-        const int li = isv ? idx - UNITS : idx;
-        const int r = li / UPR, c = li % UPR;
-        if (r < kl) {
-          const __bf16 *src = isv ? vb + (int64_t)(ks0 + r) * p.vsn : kb + (int64_t)(ks0 + r) * p.ksn;
-          stg[u] = *reinterpret_cast<const uint4 *>(src + c * 8);
-        }
-      }
-    }
-  };
-  auto lstore = [&](int buf, int kl) {
-#pragma unroll
-    for (int u = 0; u < UPT; ++u) {
-      const int idx = tid + u * NT;
-      if (idx < 2 * UNITS) {
-        const bool isv = idx >= UNITS;
-        const int li = isv ? idx - UNITS : idx;
-        const int r = li / UPR, c = li % UPR;
-        if (r < kl) {
-          __bf16 *dst = isv ? vsm + buf * NK * VP + r * VP : ksm + buf * NK * KP + r * KP;
-          *reinterpret_cast<uint4 *>(dst + c * 8) = stg[u];
-        }
-      }
+  // Issue the global -> LDS loads of keys [ks0, ks0 + kl) into buffer `buf`.
+  // Load i (< 2*NI) covers tile rows RPI*(i % NI) .. +RPI-1 of K (i < NI) or
+  // V (i >= NI); lane l writes physical chunk l % CPR of row l / CPR, which
+  // holds the logical chunk given by the tile's swizzle.
+  const int lrow = lane / CPR, lchunk = lane % CPR;
+  auto issue_loads = [&](int buf, int ks0, int kl) {
+    for (int i = wave; i < 2 * NI; i += W) {
+      const bool isv = i >= NI;
+      const int r0 = RPI * (isv ? i - NI : i);
+      if (r0 >= kl) continue;                  // wave-uniform: kl is a multiple of 16
+      const int r = r0 + lrow;
+      const int c = isv ? (lchunk ^ (2 * (r & 3))) : (lchunk ^ (r & 7));
+      const __bf16 *src = (isv ? vb + (int64_t)(ks0 + r) * p.vsn : kb + (int64_t)(ks0 + r) * p.ksn) + 8 * c;
+      const unsigned char *dst = smem + (2 * buf + (isv ? 1 : 0)) * TILEB + r0 * ROWB;
+      dma16(src, __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_uchar *)dst));
     }
   };
 
   // One chunk of NS 16-key tiles (NS = 2, or 1 for a 16-key tail) starting
-  // at key row `key0` of the LDS buffers kt/vt.
-  auto chunk = [&](auto ns_tag, const __bf16 *kt, const __bf16 *vt, int key0) {
+  // at key row `key0` of the K/V tiles kt/vt.
+  auto chunk = [&](auto fixed_tag, auto ns_tag, const unsigned char *kt, const unsigned char *vt, int key0) {
+    constexpr bool FIXED = decltype(fixed_tag)::value;
     constexpr int NS = decltype(ns_tag)::value;
     f4 s[M16][NS];
 #pragma unroll
@@ -203,12 +253,12 @@ __global__ __launch_bounds__(W * 64) void fwd_bf16_kernel(FwdParams p) {
     for (int kd = 0; kd < KD; ++kd)
 #pragma unroll
       for (int t = 0; t < NS; ++t) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8 *>(kt + (key0 + 16 * t + n16) * KP + 32 * kd + 8 * g);
+        const int r = key0 + 16 * t + n16;
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kt + r * ROWB + 16 * ((4 * kd + g) ^ (r & 7)));
 #pragma unroll
         for (int m = 0; m < M16; ++m) s[m][t] = mfma32(a, qf[m][kd], s[m][t]);
       }
-    if (!fixed) {
+    if constexpr (!FIXED) {
       // Online softmax: raise the running max where a row's chunk maximum
       // exceeds it; rescale only when some row of the wave changed.
       float mn[M16];
@@ -260,50 +310,57 @@ __global__ __launch_bounds__(W * 64) void fwd_bf16_kernel(FwdParams p) {
         for (int i = 0; i < 4; ++i) pt[m][i] = (__bf16)s[m][0][i];
       }
     }
-    const int vrow = key0 + 4 * g + (n16 >> 2), vcol = 4 * (n16 & 3);
+    // V rows of this lane's transposed reads: vr (keys 4g..4g+3 of the first
+    // 16-key tile) and vr + 16; after the swizzle a row's 32-byte segment for
+    // output tile dt sits at byte 32 * (dt ^ (row & 3)).
+    const int vr = key0 + 4 * g + (n16 >> 2);
+    const unsigned char *v0 = vt + vr * ROWB + 8 * (n16 & 3);
+    const unsigned char *v1 = v0 + 16 * ROWB;
+    const int sw = vr & 3;   // (vr + 16) & 3 == vr & 3
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       if constexpr (NS == 2) {
-        const bf16x4 lo = lds_read_tr(vt + vrow * VP + 16 * dt + vcol);
-        const bf16x4 hi = lds_read_tr(vt + (vrow + 16) * VP + 16 * dt + vcol);
+        const bf16x4 lo = lds_read_tr(v0 + 32 * (dt ^ sw));
+        const bf16x4 hi = lds_read_tr(v1 + 32 * (dt ^ sw));
         const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int m = 0; m < M16; ++m) oacc[m][dt] = mfma32(a, pk[m], oacc[m][dt]);
       } else {
-        const bf16x4 a = lds_read_tr(vt + vrow * VP + 16 * dt + vcol);
+        const bf16x4 a = lds_read_tr(v0 + 32 * (dt ^ sw));
 #pragma unroll
         for (int m = 0; m < M16; ++m) oacc[m][dt] = mfma16(a, pt[m], oacc[m][dt]);
       }
     }
   };
-  auto dispatch_step = [&](int kl, int buf) {
-    const __bf16 *kt = ksm + buf * NK * KP;
-    const __bf16 *vt = vsm + buf * NK * VP;
-    const int full = kl >> 5;
-    for (int c = 0; c < full; ++c) chunk(std::integral_constant<int, 2>{}, kt, vt, 32 * c);
-    if (kl & 16) chunk(std::integral_constant<int, 1>{}, kt, vt, kl - 16);
-  };
-
-  int cs0 = 0, ckl = 0;
-  bool have = next_step(cs0, ckl);
-  if (have) {
-    gload(cs0, ckl);
-    lstore(0, ckl);
-  }
-  __syncthreads();
-  int buf = 0;
-  while (have) {
-    int ns0 = 0, nkl = 0;
-    const bool more = next_step(ns0, nkl);
-    if (more) gload(ns0, nkl);
-    dispatch_step(ckl, buf);
-    if (more) lstore(buf ^ 1, nkl);
+  // The step loop, instantiated once per softmax path so that the two
+  // paths never merge inside it.
+  auto main_loop = [&](auto fixed_tag) {
+    int ckl = 0, cks = 0;
+    bool have = next_step(cks, ckl);
+    if (have) issue_loads(0, cks, ckl);
+    wait_vmem();
     __syncthreads();
-    buf ^= 1;
-    have = more;
-    cs0 = ns0;
-    ckl = nkl;
-  }
+    int buf = 0;
+    while (have) {
+      int nks = 0, nkl = 0;
+      const bool more = next_step(nks, nkl);
+      if (more) issue_loads(buf ^ 1, nks, nkl);
+      const unsigned char *kt = smem + (2 * buf) * TILEB;
+      const unsigned char *vt = kt + TILEB;
+      const int full = ckl >> 5;
+      for (int c = 0; c < full; ++c) chunk(fixed_tag, std::integral_constant<int, 2>{}, kt, vt, 32 * c);
+      if (ckl & 16) chunk(fixed_tag, std::integral_constant<int, 1>{}, kt, vt, ckl - 16);
+      wait_vmem();
+      __syncthreads();
+      buf ^= 1;
+      have = more;
+      ckl = nkl;
+    }
+  };
+  if (fixed)
+    main_loop(std::true_type{});
+  else
+    main_loop(std::false_type{});
 
   // Epilogue: one cross-lane reduction of the row sums, normalise, store.
 #pragma unroll
@@ -345,7 +402,7 @@ hipError_t launch_one(const FwdParams &p, const FwdConfig &c, hipStream_t st) {
                                    hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   });
   if (attr_err != hipSuccess) return attr_err;
-  hipLaunchKernelGGL(kern, dim3(p.F * p.tiles_per_frame, p.B * p.H), dim3(W * 64), c.lds_bytes, st, p);
+  hipLaunchKernelGGL(kern, dim3((unsigned)c.grid), dim3(W * 64), c.lds_bytes, st, p);
   return hipGetLastError();
 }
 
@@ -353,12 +410,11 @@ hipError_t launch_one(const FwdParams &p, const FwdConfig &c, hipStream_t st) {
 
 // (rows per wave / 16, waves per workgroup) pairs built, in order of
 // preference; the first whose workgroup tile divides the frame span wins.
-static const int kShapes[][2] = {{4, 4}, {5, 4}, {4, 3}, {5, 3}, {3, 5}, {3, 4}, {5, 2},
+static const int kShapes[][2] = {{3, 4}, {4, 4}, {3, 5}, {4, 3}, {5, 3}, {5, 4}, {5, 2},
                                  {4, 2}, {3, 3}, {3, 2}, {2, 4}, {2, 2}, {1, 1}};
 
 int fwd_bf16_lds_bytes(int nk16, int D) {
-  const int NK = nk16 * 16;
-  return 2 * NK * (D + 8) * 2 + 2 * NK * (D + 16) * 2 + kMaxRuns * 8 + 16;
+  return 4 * (nk16 * 16) * (2 * D) + kMaxRuns * 8 + 16;
 }
 
 bool choose_fwd_config(const fsattn_shape *s, const fsattn_mask *m, uint32_t flags, FwdConfig *cfg) {
@@ -401,12 +457,12 @@ bool choose_fwd_config(const fsattn_shape *s, const fsattn_mask *m, uint32_t fla
   }
 
 hipError_t launch_forward_bf16(const FwdParams &p, const FwdConfig &c, int head_dim, hipStream_t st) {
+  FSATTN_SHAPE_CASE(3, 4)
   FSATTN_SHAPE_CASE(4, 4)
-  FSATTN_SHAPE_CASE(5, 4)
+  FSATTN_SHAPE_CASE(3, 5)
   FSATTN_SHAPE_CASE(4, 3)
   FSATTN_SHAPE_CASE(5, 3)
-  FSATTN_SHAPE_CASE(3, 5)
-  FSATTN_SHAPE_CASE(3, 4)
+  FSATTN_SHAPE_CASE(5, 4)
   FSATTN_SHAPE_CASE(5, 2)
   FSATTN_SHAPE_CASE(4, 2)
   FSATTN_SHAPE_CASE(3, 3)

@@ -3,6 +3,7 @@
 // launched and no output is written.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -184,6 +185,16 @@ extern "C" fsattn_status fsattn_forward(void *hip_stream, const fsattn_shape *s,
   p.scale = scale; p.scale_log2 = scale * kLog2e;
   p.flags = flags;
   p.o_f32 = o_dtype == FSATTN_F32 ? 1 : 0;
+  // heavy frames (most live key frames) first; ties keep frame order
+  p.ordered = m->num_frames <= kMaxOrderedFrames ? 1 : 0;
+  if (p.ordered) {
+    int n = 0;
+    int64_t most = 0;
+    for (int f = 0; f < m->num_frames; ++f) most = std::max(most, live_frame_count(m, f));
+    for (int64_t c = most; c >= 1 && n < m->num_frames; --c)
+      for (int f = 0; f < m->num_frames; ++f)
+        if (live_frame_count(m, f) == c) p.frame_order[n++] = (uint8_t)f;
+  }
   const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   hipError_t e;
   if (s->dtype == FSATTN_F32) {

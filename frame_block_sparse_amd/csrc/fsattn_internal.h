@@ -50,7 +50,12 @@ struct FwdParams {
   float scale, scale_log2;
   uint32_t flags;
   int o_f32;
+  // Frames in the order their workgroups are issued (most live frames first);
+  // used when num_frames <= kMaxOrderedFrames, natural order otherwise.
+  int ordered;
+  uint8_t frame_order[64];
 };
+constexpr int kMaxOrderedFrames = 64;
 
 struct FwdConfig {
   int waves, m16, nk16;   // waves per workgroup, rows per wave / 16, keys per step / 16
