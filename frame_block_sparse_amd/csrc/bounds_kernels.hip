@@ -3,12 +3,14 @@
 // mean-centred key-norm maximum, the Cauchy-Schwarz logit bound, the window
 // term c_max of the bound audit for windowed masks, and eligibility.
 //
-// Four launches, all streaming reads of Q and K (HBM-bound):
+// Four launches; the two passes stream Q and K (HBM-bound), the other two
+// are small:
 //   pass1   per (token chunk, head): partial key sums, partial max |q|^2
-//   reduce1 per head: per-frame key sums (fixed order), key mean, max |q|^2
-//   pass2   per (token chunk, head): partial max |k - mu|^2
-//   final   per head: max |k - mu|, c_max from the frame sums, bound, gap
-//           estimate, eligibility
+//   frames  per (frame, head): the frame's key sum from its chunks
+//   pass2   per (token chunk, head): key mean from the frame sums, partial
+//           max |k - mu|^2
+//   final   per head: max |q|, max |k - mu|, c_max from the frame sums,
+//           bound, gap estimate, eligibility
 // Chunks never cross a frame, so the per-frame sums are sums of whole
 // chunks. Every reduction has a fixed order and no atomics are used, so the
 // results are bitwise reproducible run to run.
@@ -63,19 +65,6 @@ __device__ inline float block_max(float v, float *sh) {
   return r;
 }
 
-__device__ inline float block_sum(float v, float *sh) {
-  const int t = threadIdx.x;
-  sh[t] = v;
-  __syncthreads();
-  for (int o = kThreads / 2; o > 0; o >>= 1) {
-    if (t < o) sh[t] = sh[t] + sh[t + o];
-    __syncthreads();
-  }
-  const float r = sh[0];
-  __syncthreads();
-  return r;
-}
-
 // Token range [t0, t1) of chunk `c` (frame-major; chunks stay inside a frame).
 __device__ inline void chunk_range(const BoundsParams &p, int c, int *t0, int *t1) {
   const int f = c / p.chunks_per_frame, ci = c % p.chunks_per_frame;
@@ -123,27 +112,17 @@ __global__ __launch_bounds__(kThreads) void bounds_pass1(BoundsParams p) {
   if (threadIdx.x == 0) p.ws_qmax[(int64_t)bh * NC + c] = m;
 }
 
+// Per (frame, head): the frame's key sum from its chunks' partial sums, in
+// chunk order.
 template <int D>
-__global__ __launch_bounds__(kThreads) void bounds_reduce1(BoundsParams p) {
-  __shared__ float red[kThreads];
-  const int bh = blockIdx.x;
+__global__ __launch_bounds__(D) void bounds_frames(BoundsParams p) {
+  const int f = blockIdx.x, bh = blockIdx.y;
   const int NC = p.F * p.chunks_per_frame;
   const int j = threadIdx.x;
-  if (j < D) {
-    float tot = 0.f;
-    for (int f = 0; f < p.F; ++f) {
-      float s = 0.f;
-      for (int ci = 0; ci < p.chunks_per_frame; ++ci)
-        s += p.ws_part[((int64_t)bh * NC + f * p.chunks_per_frame + ci) * D + j];
-      p.ws_frame[((int64_t)bh * p.F + f) * D + j] = s;
-      tot += s;
-    }
-    p.key_mean[(int64_t)bh * D + j] = tot / (float)p.N;
-  }
-  float m = 0.f;
-  for (int c = threadIdx.x; c < NC; c += kThreads) m = fmaxf(m, p.ws_qmax[(int64_t)bh * NC + c]);
-  m = block_max(m, red);
-  if (threadIdx.x == 0) p.ws_q2[bh] = m;
+  const float *part = p.ws_part + ((int64_t)bh * NC + (int64_t)f * p.chunks_per_frame) * D + j;
+  float s = 0.f;
+  for (int ci = 0; ci < p.chunks_per_frame; ++ci) s += part[(int64_t)ci * D];
+  p.ws_frame[((int64_t)bh * p.F + f) * D + j] = s;
 }
 
 template <typename T, int D>
@@ -151,14 +130,26 @@ __global__ __launch_bounds__(kThreads) void bounds_pass2(BoundsParams p) {
   constexpr int TPR = D / 8;
   constexpr int RPP = kThreads / TPR;
   __shared__ float red[kThreads];
+  __shared__ float mu_sh[D];
   const int c = blockIdx.x, bh = blockIdx.y;
   const int b = bh / p.H, h = bh % p.H;
   const int NC = p.F * p.chunks_per_frame;
+  // key mean of the head: frame sums added in frame order, divided by N
+  // (every workgroup of the head computes the same bits; chunk 0 stores it)
+  if (threadIdx.x < D) {
+    const float *S = p.ws_frame + (int64_t)bh * p.F * D + threadIdx.x;
+    float tot = 0.f;
+    for (int f = 0; f < p.F; ++f) tot += S[(int64_t)f * D];
+    const float mu = tot / (float)p.N;
+    mu_sh[threadIdx.x] = mu;
+    if (c == 0) p.key_mean[(int64_t)bh * D + threadIdx.x] = mu;
+  }
+  __syncthreads();
   const int col = threadIdx.x % TPR, r = threadIdx.x / TPR;
   const T *k = static_cast<const T *>(p.k) + b * p.ksb + h * p.ksh + col * 8;
   float mu[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) mu[e] = p.key_mean[(int64_t)bh * D + col * 8 + e];
+  for (int e = 0; e < 8; ++e) mu[e] = mu_sh[col * 8 + e];
   int t0, t1;
   chunk_range(p, c, &t0, &t1);
   float km = 0.f;
@@ -179,35 +170,47 @@ __global__ __launch_bounds__(kThreads) void bounds_pass2(BoundsParams p) {
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void bounds_final(BoundsParams p) {
+  constexpr int PER_LANE = D / 64;
   __shared__ float red[kThreads];
   const int bh = blockIdx.x;
   const int NC = p.F * p.chunks_per_frame;
-  const int j = threadIdx.x;
-  float km = 0.f;
-  for (int c = threadIdx.x; c < NC; c += kThreads) km = fmaxf(km, p.ws_kmax[(int64_t)bh * NC + c]);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float km = 0.f, qm = 0.f;
+  for (int c = threadIdx.x; c < NC; c += kThreads) {
+    km = fmaxf(km, p.ws_kmax[(int64_t)bh * NC + c]);
+    qm = fmaxf(qm, p.ws_qmax[(int64_t)bh * NC + c]);
+  }
   km = block_max(km, red);
-  const float mu = j < D ? p.key_mean[(int64_t)bh * D + j] : 0.f;
+  qm = block_max(qm, red);
+  float mu[PER_LANE];
+#pragma unroll
+  for (int e = 0; e < PER_LANE; ++e) mu[e] = p.key_mean[(int64_t)bh * D + lane + 64 * e];
   const float *S = p.ws_frame + (int64_t)bh * p.F * D;
   // c_max: the largest distance between the mean of the keys a query frame
   // sees (its window plus the reference frame) and the head's key mean.
+  // One wave per frame; the squared distance is summed over the wave.
   float cm = 0.f;
-  for (int f = 0; f < p.F; ++f) {
+  for (int f = wave; f < p.F; f += kThreads / 64) {
     const int lo = max(0, f - p.wr), hi = min(p.F - 1, f + p.wa);
     const bool extra = p.ref >= 0 && (p.ref < lo || p.ref > hi);
+    const float cnt = (float)(hi - lo + 1 + (extra ? 1 : 0)) * (float)p.T;
     float dd = 0.f;
-    if (j < D) {
+#pragma unroll
+    for (int e = 0; e < PER_LANE; ++e) {
+      const int j = lane + 64 * e;
       float w = 0.f;
       if (extra && p.ref < lo) w += S[(int64_t)p.ref * D + j];
       for (int g = lo; g <= hi; ++g) w += S[(int64_t)g * D + j];
       if (extra && p.ref > hi) w += S[(int64_t)p.ref * D + j];
-      const float cnt = (float)(hi - lo + 1 + (extra ? 1 : 0)) * (float)p.T;
-      const float dlt = w / cnt - mu;
-      dd = dlt * dlt;
+      const float dlt = w / cnt - mu[e];
+      dd = fmaf(dlt, dlt, dd);
     }
-    cm = fmaxf(cm, block_sum(dd, red));
+    for (int o = 32; o > 0; o >>= 1) dd += __shfl_xor(dd, o, 64);
+    cm = fmaxf(cm, dd);
   }
+  cm = block_max(cm, red);
   if (threadIdx.x == 0) {
-    const float qn = sqrtf(p.ws_q2[bh]);
+    const float qn = sqrtf(qm);
     const float kn = sqrtf(km);
     const float cn = sqrtf(cm);
     fsattn_head_bound r;
@@ -227,7 +230,7 @@ hipError_t launch_all(const BoundsParams &p, hipStream_t st) {
   const int BH = p.B * p.H;
   const int NC = p.F * p.chunks_per_frame;
   hipLaunchKernelGGL((bounds_pass1<T, D>), dim3(NC, BH), dim3(kThreads), 0, st, p);
-  hipLaunchKernelGGL((bounds_reduce1<D>), dim3(BH), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL((bounds_frames<D>), dim3(p.F, BH), dim3(D), 0, st, p);
   hipLaunchKernelGGL((bounds_pass2<T, D>), dim3(NC, BH), dim3(kThreads), 0, st, p);
   hipLaunchKernelGGL((bounds_final<D>), dim3(BH), dim3(kThreads), 0, st, p);
   return hipGetLastError();

@@ -13,10 +13,12 @@
 //  * "Proving the Pixels Didn't Change": the final product PV runs in bf16 on
 //    the matrix unit (P rounded to bf16), accumulating in fp32.
 //
-// Work decomposition. A workgroup of W waves owns R = W * 16 * M16 query
-// rows of one frame of one (batch, head); all its rows share the frame's
-// key list, so each K/V step is staged once in LDS and reused by every
-// wave. A wave owns 16 * M16 rows. Per 32-key chunk of a step:
+// Work decomposition. A workgroup of W waves owns up to R = W * 16 * M16
+// query rows of one frame of one (batch, head); all its rows share the
+// frame's key list, so each K/V step is staged once in LDS and reused by
+// every wave. A wave owns 16 * M16 rows, which must divide the frame span;
+// when W wave tiles do not divide it, the frame's last workgroup has idle
+// waves (they still help stage K/V). Per 32-key chunk of a step:
 //   S^T = K Q^T      v_mfma_f32_16x16x32_bf16, A = K rows from LDS, B = Q
 //                    held in registers; lane (g = lane/16, n = lane%16)
 //                    ends with S[q = n][keys 4g..4g+3] of each 16-key tile
@@ -30,12 +32,16 @@
 //
 // Staging. K/V steps go global -> LDS with global_load_lds_dwordx4 (no
 // registers in between): each wave instruction writes 1 KB of consecutive
-// LDS, so rows are unpadded and bank conflicts are removed by an XOR
-// swizzle of 16-byte chunks instead (K: chunk ^ (row & 7), which spreads
-// the 8 rows an MFMA operand read touches per cycle; V: chunk ^ 2*(row & 3),
-// which spreads the 4 rows of a transposed read). The next step is loaded
-// into the other buffer while the current one is computed; one barrier per
-// step.
+// LDS, so rows are unpadded and bank conflicts (64 banks of 4 bytes) are
+// removed by XOR swizzles instead: K rows swizzle 16-byte chunks so that
+// the 16 rows one operand read touches fall on 16 different bank groups;
+// V rows swizzle 32-byte segments (the unit of a transposed read) so that
+// the 8 rows two lane groups read together fall on 8 different ones.
+// NBUF buffers form a ring:
+// while step s is computed, steps s+1 .. s+NBUF-1 are in flight. Every step
+// issues the same number of copies per wave (a short step re-reads its last
+// valid row), so each wave waits only for its own copies of step s with a
+// constant vmcnt, and one barrier per step publishes them to all waves.
 //
 // Order. Workgroups are issued heavy frames first (frames seeing the most
 // key frames), and the (frame, head) groups are dealt round-robin to the 8
@@ -82,8 +88,16 @@ __device__ inline bf16x4 lds_read_tr(const unsigned char *p) {
 // behind the in-flight prefetch; completion is awaited explicitly
 // (wait_vmem() before the step barrier). M0 carries the LDS base; no
 // other code in these kernels uses M0.
-__device__ inline void dma16(const void *src, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
+// The address is a wave-uniform 64-bit base (SGPR pair) plus a 32-bit
+// per-lane byte offset.
+__device__ inline void dma16(uint64_t base, unsigned off, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory");
+}
+__device__ inline uint64_t uniform_ptr(const void *p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // s_waitcnt vmcnt(0) through the builtin, which the compiler's own wait
@@ -91,6 +105,13 @@ __device__ inline void dma16(const void *src, unsigned lds) {
 // memory load is considered outstanding, so no wait for an earlier load is
 // sunk into the step loop, where it would also stall on the prefetch.
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// s_waitcnt vmcnt(N) (other counters unconstrained), N < 64.
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // Workgroup index -> (frame, batch*head, tile within the frame).
 __device__ inline void map_block(const FwdParams &p, int bid, int &f, int &bh, int &tile) {
@@ -122,8 +143,13 @@ __device__ inline void map_block(const FwdParams &p, int bid, int &f, int &bh, i
   f = p.ordered ? p.frame_order[fr] : fr;
 }
 
-template <int M16, int W, int NK16, int D>
-__global__ __launch_bounds__(W * 64) void fwd_bf16_kernel(FwdParams p) {
+// Waves per SIMD the register budget is held to: 3 for 32-row waves, 2 for
+// 48-row waves, 1 above.
+constexpr int fwd_min_waves(int m16) { return m16 <= 2 ? 3 : (m16 == 3 ? 2 : 1); }
+
+template <int M16, int W, int NK16, int NBUF, int D>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(fwd_min_waves(M16))))
+void fwd_bf16_kernel(FwdParams p) {
   constexpr int NK = NK16 * 16;
   constexpr int KD = D / 32;          // 32-wide slices of d for QK^T
   constexpr int DT = D / 16;          // 16-wide output column tiles for PV
@@ -132,10 +158,18 @@ __global__ __launch_bounds__(W * 64) void fwd_bf16_kernel(FwdParams p) {
   constexpr int RPI = 1024 / ROWB;    // rows written by one wave-wide 16-byte load
   constexpr int NI = NK / RPI;        // such loads per tile
   constexpr int CPR = D / 8;          // 16-byte chunks per row
+  // swizzles: K chunk c of row r lives at chunk c ^ ksw(r); V 32-byte
+  // segment s of row r lives at segment s ^ vsw(r). Rows are 256 bytes for
+  // d = 128 (one full bank row), 128 bytes for d = 64 (two rows per bank row).
+  auto ksw = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+  auto vsw = [](int r) { return D == 128 ? (r & 7) : ((r >> 1) & 3); };
+  constexpr int LPW = 2 * NI / W;     // copies per wave per step
+  static_assert(NI % W == 0, "copies must split evenly over the waves");
+  static_assert((NBUF & (NBUF - 1)) == 0 && NBUF >= 2, "ring size is a power of two");
 
   extern __shared__ __align__(16) unsigned char smem[];
-  // [buf 0: K tile, V tile][buf 1: K tile, V tile], then the runs
-  int2 *runs = reinterpret_cast<int2 *>(smem + 4 * TILEB);
+  // NBUF x [K tile, V tile], then the runs
+  int2 *runs = reinterpret_cast<int2 *>(smem + 2 * NBUF * TILEB);
   int *nruns_sm = reinterpret_cast<int *>(runs + kMaxRuns);
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -145,6 +179,7 @@ __global__ __launch_bounds__(W * 64) void fwd_bf16_kernel(FwdParams p) {
   map_block(p, blockIdx.x, f, bh, ti);
   const int b = bh / p.H, h = bh % p.H;
   const int row0 = f * p.T + ti * p.rows_per_wg;
+  const bool active = row0 + wave * 16 * M16 < (f + 1) * p.T;   // wave-uniform
   if (wave == 0) build_runs(p.row_ptr, p.col_idx, p.nnz, row0 / p.bq, p.bk, p.N, runs, nruns_sm);
 
   const __bf16 *qb = static_cast<const __bf16 *>(p.q) + b * p.qsb + h * p.qsh;
@@ -154,12 +189,15 @@ __global__ __launch_bounds__(W * 64) void fwd_bf16_kernel(FwdParams p) {
 
   // Q fragments (B operand of S^T = K Q^T): row n16 of each 16-row group,
   // d = 32*kd + 8*g .. +7.
+  // An idle wave reads its workgroup's first rows instead (always in range)
+  // and never stores.
+  const int qrow0 = active ? wrow0 : row0;
   bf16x8 qf[M16][KD];
 #pragma unroll
   for (int m = 0; m < M16; ++m)
 #pragma unroll
     for (int kd = 0; kd < KD; ++kd)
-      qf[m][kd] = *reinterpret_cast<const bf16x8 *>(qb + (int64_t)(wrow0 + 16 * m + n16) * p.qsn +
+      qf[m][kd] = *reinterpret_cast<const bf16x8 *>(qb + (int64_t)(qrow0 + 16 * m + n16) * p.qsn +
                                                      32 * kd + 8 * g);
   wait_vmem();
 
@@ -205,37 +243,55 @@ __global__ __launch_bounds__(W * 64) void fwd_bf16_kernel(FwdParams p) {
 
   __syncthreads();
   const int nr = *nruns_sm;
-  int ri = 0, roff = 0;
-  auto next_step = [&](int &ks0, int &kl) -> bool {
-    while (ri < nr) {
-      const int s0 = runs[ri].x, s1 = runs[ri].y;
-      if (s0 + roff < s1) {
-        ks0 = s0 + roff;
-        kl = min(NK, s1 - ks0);
-        roff += kl;
-        return true;
-      }
-      ++ri;
-      roff = 0;
+  // Step iterator over the runs: next step's first key and length. Each
+  // iterator keeps its current run's bounds in scalar registers and reads
+  // the run table only when it moves to the next run. The loads run
+  // NBUF-1 steps ahead of the compute, each with its own iterator.
+  struct Iter {
+    int ri, pos, end;
+  };
+  auto iter_init = [&](Iter &it) {
+    it.ri = 0;
+    it.pos = nr > 0 ? __builtin_amdgcn_readfirstlane(runs[0].x) : 0;
+    it.end = nr > 0 ? __builtin_amdgcn_readfirstlane(runs[0].y) : 0;
+  };
+  auto next_step = [&](Iter &it, int &ks0, int &kl) -> bool {
+    while (it.pos >= it.end) {
+      if (++it.ri >= nr) return false;
+      it.pos = __builtin_amdgcn_readfirstlane(runs[it.ri].x);
+      it.end = __builtin_amdgcn_readfirstlane(runs[it.ri].y);
     }
-    return false;
+    ks0 = it.pos;
+    kl = min(NK, it.end - it.pos);
+    it.pos += kl;
+    return true;
   };
 
-  // Issue the global -> LDS loads of keys [ks0, ks0 + kl) into buffer `buf`.
-  // Load i (< 2*NI) covers tile rows RPI*(i % NI) .. +RPI-1 of K (i < NI) or
-  // V (i >= NI); lane l writes physical chunk l % CPR of row l / CPR, which
-  // holds the logical chunk given by the tile's swizzle.
+  // Global -> LDS copies. A tile of NK rows is NI wave-wide copies of RPI
+  // rows; wave w issues copies w, w + W, ... of K, then the same of V
+  // (NI is a multiple of W). Lane l writes physical chunk l % CPR of row
+  // RPI*copy + l / CPR, which holds the logical chunk given by the tile's
+  // swizzle; its source offset within the step is fixed, so it is computed
+  // once (rows past a short step re-read the step's last row).
+  constexpr int CPT = NI / W;         // copies per wave per tile
   const int lrow = lane / CPR, lchunk = lane % CPR;
+  // Byte offsets within a step are 32-bit (the host guarantees that 64 rows
+  // of either tensor span less than 2^31 bytes).
+  const unsigned kstride2 = (unsigned)(2 * p.ksn), vstride2 = (unsigned)(2 * p.vsn);
+  const unsigned lds_base = (unsigned)(uintptr_t)(lds_uchar *)smem;
   auto issue_loads = [&](int buf, int ks0, int kl) {
-    for (int i = wave; i < 2 * NI; i += W) {
-      const bool isv = i >= NI;
-      const int r0 = RPI * (isv ? i - NI : i);
-      if (r0 >= kl) continue;                  // wave-uniform: kl is a multiple of 16
-      const int r = r0 + lrow;
-      const int c = isv ? (lchunk ^ (2 * (r & 3))) : (lchunk ^ (r & 7));
-      const __bf16 *src = (isv ? vb + (int64_t)(ks0 + r) * p.vsn : kb + (int64_t)(ks0 + r) * p.ksn) + 8 * c;
-      const unsigned char *dst = smem + (2 * buf + (isv ? 1 : 0)) * TILEB + r0 * ROWB;
-      dma16(src, __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_uchar *)dst));
+    const uint64_t ksrc = uniform_ptr(kb + (int64_t)ks0 * p.ksn);
+    const uint64_t vsrc = uniform_ptr(vb + (int64_t)ks0 * p.vsn);
+    const unsigned kdst = lds_base + 2 * buf * TILEB;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      const int r = RPI * (wave + j * W) + lrow;
+      const unsigned rs = (unsigned)min(r, kl - 1);
+      const unsigned ck = lchunk ^ ksw(r);
+      const unsigned cv = (((lchunk >> 1) ^ vsw(r)) << 1) | (lchunk & 1);
+      const unsigned row0b = (unsigned)(RPI * (wave + j * W) * ROWB);
+      dma16(ksrc, rs * kstride2 + 16u * ck, __builtin_amdgcn_readfirstlane(kdst + row0b));
+      dma16(vsrc, rs * vstride2 + 16u * cv, __builtin_amdgcn_readfirstlane(kdst + TILEB + row0b));
     }
   };
 
@@ -254,7 +310,7 @@ __global__ __launch_bounds__(W * 64) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int t = 0; t < NS; ++t) {
         const int r = key0 + 16 * t + n16;
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kt + r * ROWB + 16 * ((4 * kd + g) ^ (r & 7)));
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kt + r * ROWB + 16 * ((4 * kd + g) ^ ksw(r)));
 #pragma unroll
         for (int m = 0; m < M16; ++m) s[m][t] = mfma32(a, qf[m][kd], s[m][t]);
       }
@@ -312,11 +368,11 @@ __global__ __launch_bounds__(W * 64) void fwd_bf16_kernel(FwdParams p) {
     }
     // V rows of this lane's transposed reads: vr (keys 4g..4g+3 of the first
     // 16-key tile) and vr + 16; after the swizzle a row's 32-byte segment for
-    // output tile dt sits at byte 32 * (dt ^ (row & 3)).
+    // output tile dt sits at byte 32 * (dt ^ vsw(row)).
     const int vr = key0 + 4 * g + (n16 >> 2);
     const unsigned char *v0 = vt + vr * ROWB + 8 * (n16 & 3);
     const unsigned char *v1 = v0 + 16 * ROWB;
-    const int sw = vr & 3;   // (vr + 16) & 3 == vr & 3
+    const int sw = vsw(vr);   // vsw(vr + 16) == vsw(vr)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       if constexpr (NS == 2) {
@@ -335,26 +391,43 @@ __global__ __launch_bounds__(W * 64) void fwd_bf16_kernel(FwdParams p) {
   // The step loop, instantiated once per softmax path so that the two
   // paths never merge inside it.
   auto main_loop = [&](auto fixed_tag) {
-    int ckl = 0, cks = 0;
-    bool have = next_step(cks, ckl);
-    if (have) issue_loads(0, cks, ckl);
-    wait_vmem();
-    __syncthreads();
-    int buf = 0;
-    while (have) {
-      int nks = 0, nkl = 0;
-      const bool more = next_step(nks, nkl);
-      if (more) issue_loads(buf ^ 1, nks, nkl);
-      const unsigned char *kt = smem + (2 * buf) * TILEB;
+    Iter li, ci;
+    iter_init(li);
+    iter_init(ci);
+    int issued = 0;
+#pragma unroll
+    for (int j = 0; j < NBUF - 1; ++j) {
+      int ks = 0, kl = 0;
+      if (next_step(li, ks, kl)) {
+        issue_loads(j, ks, kl);
+        ++issued;
+      }
+    }
+    int step = 0, cks = 0, ckl = 0;
+    while (next_step(ci, cks, ckl)) {
+      // my copies of this step are done once at most (issued - step - 1)
+      // later steps' copies are outstanding
+      const int later = issued - step - 1;
+      if (later >= NBUF - 1) wait_vmcnt<(NBUF - 1) * LPW>();
+      else if (NBUF > 3 && later == 2) wait_vmcnt<(NBUF > 3 ? 2 * LPW : 0)>();
+      else if (NBUF > 2 && later == 1) wait_vmcnt<(NBUF > 2 ? LPW : 0)>();
+      else wait_vmem();
+      __syncthreads();   // every wave's copies of this step landed; step-1 is free
+      {
+        int ks = 0, kl = 0;
+        if (next_step(li, ks, kl)) {
+          issue_loads((step + NBUF - 1) & (NBUF - 1), ks, kl);
+          ++issued;
+        }
+      }
+      const unsigned char *kt = smem + 2 * (step & (NBUF - 1)) * TILEB;
       const unsigned char *vt = kt + TILEB;
-      const int full = ckl >> 5;
-      for (int c = 0; c < full; ++c) chunk(fixed_tag, std::integral_constant<int, 2>{}, kt, vt, 32 * c);
-      if (ckl & 16) chunk(fixed_tag, std::integral_constant<int, 1>{}, kt, vt, ckl - 16);
-      wait_vmem();
-      __syncthreads();
-      buf ^= 1;
-      have = more;
-      ckl = nkl;
+      if (active) {
+        const int full = ckl >> 5;
+        for (int c = 0; c < full; ++c) chunk(fixed_tag, std::integral_constant<int, 2>{}, kt, vt, 32 * c);
+        if (ckl & 16) chunk(fixed_tag, std::integral_constant<int, 1>{}, kt, vt, ckl - 16);
+      }
+      ++step;
     }
   };
   if (fixed)
@@ -362,6 +435,7 @@ __global__ __launch_bounds__(W * 64) void fwd_bf16_kernel(FwdParams p) {
   else
     main_loop(std::false_type{});
 
+  if (!active) return;
   // Epilogue: one cross-lane reduction of the row sums, normalise, store.
 #pragma unroll
   for (int m = 0; m < M16; ++m) {
@@ -392,9 +466,17 @@ __global__ __launch_bounds__(W * 64) void fwd_bf16_kernel(FwdParams p) {
   }
 }
 
+// Copies of one K (or V) tile per step: NK rows of 2*D bytes, 1 KB each.
+constexpr int copies_per_tile(int nk16, int D) { return nk16 * 16 * 2 * D / 1024; }
+
 template <int M16, int W, int NK16, int D>
 hipError_t launch_one(const FwdParams &p, const FwdConfig &c, hipStream_t st) {
-  auto kern = fwd_bf16_kernel<M16, W, NK16, D>;
+  if constexpr (copies_per_tile(NK16, D) % W != 0) {
+    return hipErrorInvalidValue;   // never chosen: choose_fwd_config skips it
+  } else {
+  // 32-key steps use a ring of 4 buffers, 64-key steps a ring of 2
+  constexpr int NBUF = NK16 == 2 ? 4 : 2;
+  auto kern = fwd_bf16_kernel<M16, W, NK16, NBUF, D>;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [&] {
@@ -404,17 +486,19 @@ hipError_t launch_one(const FwdParams &p, const FwdConfig &c, hipStream_t st) {
   if (attr_err != hipSuccess) return attr_err;
   hipLaunchKernelGGL(kern, dim3((unsigned)c.grid), dim3(W * 64), c.lds_bytes, st, p);
   return hipGetLastError();
+  }
 }
 
 }  // namespace
 
 // (rows per wave / 16, waves per workgroup) pairs built, in order of
-// preference; the first whose workgroup tile divides the frame span wins.
-static const int kShapes[][2] = {{3, 4}, {4, 4}, {3, 5}, {4, 3}, {5, 3}, {5, 4}, {5, 2},
-                                 {4, 2}, {3, 3}, {3, 2}, {2, 4}, {2, 2}, {1, 1}};
+// preference; the first whose wave tile (16 * M16 rows) divides the frame
+// span wins.
+static const int kShapes[][2] = {{3, 4}, {2, 8}, {4, 4}, {2, 4}, {1, 4}, {3, 2}, {4, 2}, {2, 2}};
 
 int fwd_bf16_lds_bytes(int nk16, int D) {
-  return 4 * (nk16 * 16) * (2 * D) + kMaxRuns * 8 + 16;
+  const int nbuf = nk16 == 2 ? 4 : 2;
+  return nbuf * 2 * (nk16 * 16) * (2 * D) + kMaxRuns * 8 + 16;
 }
 
 bool choose_fwd_config(const fsattn_shape *s, const fsattn_mask *m, uint32_t flags, FwdConfig *cfg) {
@@ -430,18 +514,19 @@ bool choose_fwd_config(const fsattn_shape *s, const fsattn_mask *m, uint32_t fla
     return true;
   }
   const int wo = (flags >> 8) & 15, mo = (flags >> 12) & 15, so = (flags >> 16) & 15;
-  const int nk16 = so ? so : 4;
+  const int nk16 = so ? so : 2;
   if (nk16 != 2 && nk16 != 4) return false;
   for (const auto &sh : kShapes) {
     const int m16 = sh[0], w = sh[1];
     if ((wo && w != wo) || (mo && m16 != mo)) continue;
-    const int R = 16 * m16 * w;
-    if (T % R) continue;
+    if (T % (16 * m16)) continue;
+    if (copies_per_tile(nk16, s->head_dim) % w) continue;
+    const int wave_tiles = T / (16 * m16);
     cfg->waves = w;
     cfg->m16 = m16;
     cfg->nk16 = nk16;
     cfg->lds_bytes = fwd_bf16_lds_bytes(nk16, s->head_dim);
-    cfg->grid = (int64_t)m->num_frames * (T / R) * BH;
+    cfg->grid = (int64_t)m->num_frames * ((wave_tiles + w - 1) / w) * BH;
     return true;
   }
   return false;
@@ -458,18 +543,13 @@ bool choose_fwd_config(const fsattn_shape *s, const fsattn_mask *m, uint32_t fla
 
 hipError_t launch_forward_bf16(const FwdParams &p, const FwdConfig &c, int head_dim, hipStream_t st) {
   FSATTN_SHAPE_CASE(3, 4)
+  FSATTN_SHAPE_CASE(2, 8)
   FSATTN_SHAPE_CASE(4, 4)
-  FSATTN_SHAPE_CASE(3, 5)
-  FSATTN_SHAPE_CASE(4, 3)
-  FSATTN_SHAPE_CASE(5, 3)
-  FSATTN_SHAPE_CASE(5, 4)
-  FSATTN_SHAPE_CASE(5, 2)
-  FSATTN_SHAPE_CASE(4, 2)
-  FSATTN_SHAPE_CASE(3, 3)
-  FSATTN_SHAPE_CASE(3, 2)
   FSATTN_SHAPE_CASE(2, 4)
+  FSATTN_SHAPE_CASE(1, 4)
+  FSATTN_SHAPE_CASE(3, 2)
+  FSATTN_SHAPE_CASE(4, 2)
   FSATTN_SHAPE_CASE(2, 2)
-  FSATTN_SHAPE_CASE(1, 1)
   return hipErrorInvalidValue;
 }
 

@@ -39,7 +39,7 @@ fsattn_status check_tensor(const fsattn_tensor &t, int esz, int head_dim) {
 }
 
 struct WsLayout {
-  size_t part, frame, qmax, kmax, q2, total;
+  size_t part, frame, qmax, kmax, total;
   int chunks_per_frame;
 };
 
@@ -56,7 +56,6 @@ WsLayout ws_layout(const fsattn_shape *s, const fsattn_mask *m) {
   w.frame = off; off = align256(off + sizeof(float) * BH * m->num_frames * D);
   w.qmax = off;  off = align256(off + sizeof(float) * BH * NC);
   w.kmax = off;  off = align256(off + sizeof(float) * BH * NC);
-  w.q2 = off;    off = align256(off + sizeof(float) * BH);
   w.total = off;
   return w;
 }
@@ -113,7 +112,6 @@ extern "C" fsattn_status fsattn_head_bounds(void *hip_stream, const fsattn_shape
   p.ws_frame = reinterpret_cast<float *>(base + w.frame);
   p.ws_qmax = reinterpret_cast<float *>(base + w.qmax);
   p.ws_kmax = reinterpret_cast<float *>(base + w.kmax);
-  p.ws_q2 = reinterpret_cast<float *>(base + w.q2);
   const hipError_t e = launch_head_bounds(p, s->dtype, static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? FSATTN_OK : FSATTN_ERR_HIP;
 }
@@ -165,6 +163,11 @@ extern "C" fsattn_status fsattn_forward(void *hip_stream, const fsattn_shape *s,
   if (o_dtype != s->dtype && o_dtype != FSATTN_F32) return FSATTN_ERR_UNSUPPORTED;
   if ((st = check_tensor(o, elem_size(o_dtype), s->head_dim)) != FSATTN_OK) return st;
   if (!row_ptr || !col_idx) return FSATTN_ERR_INVALID_ARGUMENT;
+  // the bf16 kernel addresses one staged step (at most 64 rows) with 32-bit
+  // byte offsets from the step's first row
+  if (s->dtype == FSATTN_BF16 &&
+      (k.stride_n * esz * 64 >= ((int64_t)1 << 31) || v.stride_n * esz * 64 >= ((int64_t)1 << 31)))
+    return FSATTN_ERR_UNSUPPORTED;
   int64_t nqb = 0, want_nnz = 0;
   if ((st = fsattn_plan_size(m, &nqb, &want_nnz)) != FSATTN_OK) return st;
   if (nnz != want_nnz) return FSATTN_ERR_INVALID_ARGUMENT;
@@ -203,7 +206,7 @@ extern "C" fsattn_status fsattn_forward(void *hip_stream, const fsattn_shape *s,
     e = launch_forward_f32(p, s->head_dim, stream);
   } else {
     p.rows_per_wg = 16 * cfg.m16 * cfg.waves;
-    p.tiles_per_frame = p.T / p.rows_per_wg;
+    p.tiles_per_frame = (p.T + p.rows_per_wg - 1) / p.rows_per_wg;
     e = launch_forward_bf16(p, cfg, s->head_dim, stream);
   }
   return e == hipSuccess ? FSATTN_OK : FSATTN_ERR_HIP;

@@ -31,7 +31,6 @@ struct BoundsParams {
   float *ws_frame;    // [BH][F][D]  per-frame key sums
   float *ws_qmax;     // [BH][NC]    partial max |q|^2
   float *ws_kmax;     // [BH][NC]    partial max |k - mu|^2
-  float *ws_q2;       // [BH]        max |q|^2
 };
 
 hipError_t launch_head_bounds(const BoundsParams &p, int dtype, hipStream_t st);

@@ -157,15 +157,18 @@ def test_launch_info_choices():
     for i in (2, 3, 4, 5):
         w = workloads.config(i)
         waves, rows, kstep, wgs, lds = fs.launch_info((w.batch, w.heads, w.seq_len, w.head_dim), fs.BF16, w)
-        assert w.tokens_per_frame % (waves * rows) == 0
-        assert wgs == w.batch * w.heads * w.seq_len // (waves * rows)
+        assert w.tokens_per_frame % rows == 0                  # a wave tile never straddles frames
+        tiles = -(-w.tokens_per_frame // (waves * rows))       # the last tile of a frame may be ragged
+        assert wgs == w.batch * w.heads * w.num_frames * tiles
         assert lds <= 160 * 1024
     w = workloads.config(3)
-    with pytest.raises(fs.FsattnError) as e:      # 4 waves x 64 rows does not divide 3600
+    with pytest.raises(fs.FsattnError) as e:      # 64-row wave tiles do not divide 3600
         fs.launch_info((1, 5, 32400, 128), fs.BF16, w, fs.make_flags(waves=4, rows_per_wave=64))
     assert e.value.status == 3
-    waves, rows, _, _, _ = fs.launch_info((1, 5, 32400, 128), fs.BF16, w, fs.make_flags(waves=5, rows_per_wave=48))
-    assert (waves, rows) == (5, 48)
+    waves, rows, _, _, _ = fs.launch_info((1, 5, 32400, 128), fs.BF16, w, fs.make_flags(waves=2, rows_per_wave=48))
+    assert (waves, rows) == (2, 48)
+    with pytest.raises(fs.FsattnError):           # 5-wave workgroups are not built
+        fs.launch_info((1, 5, 32400, 128), fs.BF16, w, fs.make_flags(waves=5, rows_per_wave=48))
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

@@ -114,8 +114,7 @@ SMALL = [
 ]
 
 # (waves, rows per wave) of every built launch shape, and the key steps
-SHAPES = [(4, 64), (4, 80), (3, 64), (3, 80), (5, 48), (4, 48), (2, 80), (2, 64), (3, 48), (2, 48),
-          (4, 32), (2, 32), (1, 16)]
+SHAPES = [(4, 48), (8, 32), (4, 64), (4, 32), (4, 16), (2, 48), (2, 64), (2, 32)]
 SHAPE_OVERRIDES = [(w, r, ks) for (w, r) in SHAPES for ks in (32, 64)]
 
 
@@ -148,9 +147,10 @@ _SHAPE_REF = {}
 
 @pytest.mark.parametrize("shape", SHAPE_OVERRIDES, ids=[f"w{a}_r{b}_k{c}" for a, b, c in SHAPE_OVERRIDES])
 def test_forward_launch_shapes(dev, shape):
-    """Every built launch shape, on a frame span its workgroup tile divides."""
+    """Every built launch shape on a frame span its wave tile divides; several
+    leave the frame's last workgroup ragged (idle waves)."""
     waves, rows, kstep = shape
-    T = next(t for t in (960, 768, 720) if t % (waves * rows) == 0)
+    T = next(t for t in (720, 960, 768) if t % rows == 0)
     case = (f"shapes{T}", 1, 2, 3, T, 128, "bf16", 1, 1, 0, 48, 48)
     w, q, k, v = _small(case, seed=2)
     if T not in _SHAPE_REF:
