@@ -81,11 +81,15 @@ def cpu_baseline(w, q, k, v, budget_s: float):
         oracle.attention_ref(q, k, v, g, rows=rows)
         return time.perf_counter() - t0
 
-    rows = sample(2)
-    t = timed(rows)
-    per_frame = max(2, min(g.T, int(2 * budget_s / max(t, 1e-3))))
+    per_frame = 2
     rows = sample(per_frame)
     t = timed(rows)
+    # grow the sample until it takes about the budget (per-call overheads make
+    # the first small samples underestimate the rate)
+    while t < 0.5 * budget_s and per_frame < g.T:
+        per_frame = max(per_frame + 1, min(g.T, int(per_frame * 0.8 * budget_s / max(t, 1e-3))))
+        rows = sample(per_frame)
+        t = timed(rows)
     flops = sum(4 * w.head_dim * live_keys_per_row[int(r) // g.T] for r in rows) * w.batch * w.heads
     try:
         from threadpoolctl import threadpool_info
@@ -107,9 +111,16 @@ def main():
     ap.add_argument("--waves", type=int, default=0)
     ap.add_argument("--rows", type=int, default=0)
     ap.add_argument("--kstep", type=int, default=0)
+    ap.add_argument("--ring", type=int, default=0)
     ap.add_argument("--mode", default="auto", choices=["auto", "online", "fixed"])
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
+    ap.add_argument("--prewarm-seconds", type=float, default=1.0,
+                    help="untimed forward launches before the warmup steps, so that the GPU clocks have "
+                         "ramped up after the host-side input generation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device-to-device copy of 512 MiB three times (the known-size "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -129,6 +140,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        nbytes = 512 << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": nbytes, "launches": 3}), flush=True)
+        return
     fs.lib()
     w = workloads.config(args.workload)
     print(f"[bench] workload {args.workload} {w.name}: generating inputs", file=sys.stderr, flush=True)
@@ -138,7 +158,7 @@ def main():
     od = torch.empty_like(qd)
     mask = F.to_mask(w)
     nqb, nnz = fs.plan_size(mask)
-    flags = fs.make_flags(args.mode, waves=args.waves, rows_per_wave=args.rows, key_step=args.kstep)
+    flags = fs.make_flags(args.mode, waves=args.waves, rows_per_wave=args.rows, key_step=args.kstep, ring=args.ring)
     waves, rows_pw, kstep, wgs, lds = fs.launch_info(tuple(qd.shape), fs.BF16 if w.dtype == "bf16" else fs.F32,
                                                      mask, flags)
     live_flops = 4.0 * w.head_dim * w.batch * w.heads * nnz * w.block_q * w.block_k
@@ -178,7 +198,13 @@ def main():
         fs.forward(qd, kd, vd, dplan, bnd, flags=flags, out=od)
         e2.record()
 
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    print(f"[bench] prewarm {args.prewarm_seconds} s, warmup {args.warmup}", file=sys.stderr, flush=True)
+    step(0)
+    torch.cuda.synchronize()
+    t_pre = time.perf_counter()
+    while time.perf_counter() - t_pre < args.prewarm_seconds:
+        fs.forward(qd, kd, vd, dplan, bnd, flags=flags, out=od)
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -213,6 +239,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "prewarm_s": args.prewarm_seconds,
         "config": {
             "workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
             "head_dim": w.head_dim, "frames": w.num_frames, "tokens_per_frame": w.tokens_per_frame,

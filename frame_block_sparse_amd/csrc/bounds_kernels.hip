@@ -65,6 +65,22 @@ __device__ inline float block_max(float v, float *sh) {
   return r;
 }
 
+// sum_{i < n} x[i * stride], added in index order, with up to 8 loads in
+// flight (the order of the additions is the plain sequential one).
+__device__ inline float ordered_sum(const float *x, int n, int64_t stride) {
+  float s = 0.f;
+  int i = 0;
+  for (; i + 8 <= n; i += 8) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = x[(int64_t)(i + e) * stride];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += v[e];
+  }
+  for (; i < n; ++i) s += x[(int64_t)i * stride];
+  return s;
+}
+
 // Token range [t0, t1) of chunk `c` (frame-major; chunks stay inside a frame).
 __device__ inline void chunk_range(const BoundsParams &p, int c, int *t0, int *t1) {
   const int f = c / p.chunks_per_frame, ci = c % p.chunks_per_frame;
@@ -120,9 +136,7 @@ __global__ __launch_bounds__(D) void bounds_frames(BoundsParams p) {
   const int NC = p.F * p.chunks_per_frame;
   const int j = threadIdx.x;
   const float *part = p.ws_part + ((int64_t)bh * NC + (int64_t)f * p.chunks_per_frame) * D + j;
-  float s = 0.f;
-  for (int ci = 0; ci < p.chunks_per_frame; ++ci) s += part[(int64_t)ci * D];
-  p.ws_frame[((int64_t)bh * p.F + f) * D + j] = s;
+  p.ws_frame[((int64_t)bh * p.F + f) * D + j] = ordered_sum(part, p.chunks_per_frame, D);
 }
 
 template <typename T, int D>
@@ -138,9 +152,7 @@ __global__ __launch_bounds__(kThreads) void bounds_pass2(BoundsParams p) {
   // (every workgroup of the head computes the same bits; chunk 0 stores it)
   if (threadIdx.x < D) {
     const float *S = p.ws_frame + (int64_t)bh * p.F * D + threadIdx.x;
-    float tot = 0.f;
-    for (int f = 0; f < p.F; ++f) tot += S[(int64_t)f * D];
-    const float mu = tot / (float)p.N;
+    const float mu = ordered_sum(S, p.F, D) / (float)p.N;
     mu_sh[threadIdx.x] = mu;
     if (c == 0) p.key_mean[(int64_t)bh * D + threadIdx.x] = mu;
   }
@@ -168,24 +180,31 @@ __global__ __launch_bounds__(kThreads) void bounds_pass2(BoundsParams p) {
   if (threadIdx.x == 0) p.ws_kmax[(int64_t)bh * NC + c] = m;
 }
 
+constexpr int kFinalLdsFloats = 12288;   // frame sums staged in LDS up to this size (48 KB)
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void bounds_final(BoundsParams p) {
   constexpr int PER_LANE = D / 64;
   __shared__ float red[kThreads];
+  __shared__ float S_sh[kFinalLdsFloats];
   const int bh = blockIdx.x;
   const int NC = p.F * p.chunks_per_frame;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float *Sg = p.ws_frame + (int64_t)bh * p.F * D;
+  const bool staged = p.F * D <= kFinalLdsFloats;
+  if (staged)
+    for (int i = threadIdx.x; i < p.F * D; i += kThreads) S_sh[i] = Sg[i];
   float km = 0.f, qm = 0.f;
   for (int c = threadIdx.x; c < NC; c += kThreads) {
     km = fmaxf(km, p.ws_kmax[(int64_t)bh * NC + c]);
     qm = fmaxf(qm, p.ws_qmax[(int64_t)bh * NC + c]);
   }
-  km = block_max(km, red);
+  km = block_max(km, red);   // (its barriers also publish S_sh)
   qm = block_max(qm, red);
   float mu[PER_LANE];
 #pragma unroll
   for (int e = 0; e < PER_LANE; ++e) mu[e] = p.key_mean[(int64_t)bh * D + lane + 64 * e];
-  const float *S = p.ws_frame + (int64_t)bh * p.F * D;
+  const float *S = staged ? S_sh : Sg;
   // c_max: the largest distance between the mean of the keys a query frame
   // sees (its window plus the reference frame) and the head's key mean.
   // One wave per frame; the squared distance is summed over the wave.
@@ -200,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void bounds_final(BoundsParams p) {
       const int j = lane + 64 * e;
       float w = 0.f;
       if (extra && p.ref < lo) w += S[(int64_t)p.ref * D + j];
-      for (int g = lo; g <= hi; ++g) w += S[(int64_t)g * D + j];
+      w += ordered_sum(S + (int64_t)lo * D + j, hi - lo + 1, D);
       if (extra && p.ref > hi) w += S[(int64_t)p.ref * D + j];
       const float dlt = w / cnt - mu[e];
       dd = fmaf(dlt, dlt, dd);

@@ -165,7 +165,7 @@ void fwd_bf16_kernel(FwdParams p) {
   auto vsw = [](int r) { return D == 128 ? (r & 7) : ((r >> 1) & 3); };
   constexpr int LPW = 2 * NI / W;     // copies per wave per step
   static_assert(NI % W == 0, "copies must split evenly over the waves");
-  static_assert((NBUF & (NBUF - 1)) == 0 && NBUF >= 2, "ring size is a power of two");
+  static_assert(NBUF >= 2, "ring of at least two buffers");
 
   extern __shared__ __align__(16) unsigned char smem[];
   // NBUF x [K tile, V tile], then the runs
@@ -416,11 +416,11 @@ void fwd_bf16_kernel(FwdParams p) {
       {
         int ks = 0, kl = 0;
         if (next_step(li, ks, kl)) {
-          issue_loads((step + NBUF - 1) & (NBUF - 1), ks, kl);
+          issue_loads((step + NBUF - 1) % NBUF, ks, kl);
           ++issued;
         }
       }
-      const unsigned char *kt = smem + 2 * (step & (NBUF - 1)) * TILEB;
+      const unsigned char *kt = smem + 2 * (step % NBUF) * TILEB;
       const unsigned char *vt = kt + TILEB;
       if (active) {
         const int full = ckl >> 5;
@@ -469,13 +469,11 @@ void fwd_bf16_kernel(FwdParams p) {
 // Copies of one K (or V) tile per step: NK rows of 2*D bytes, 1 KB each.
 constexpr int copies_per_tile(int nk16, int D) { return nk16 * 16 * 2 * D / 1024; }
 
-template <int M16, int W, int NK16, int D>
+template <int M16, int W, int NK16, int NBUF, int D>
 hipError_t launch_one(const FwdParams &p, const FwdConfig &c, hipStream_t st) {
   if constexpr (copies_per_tile(NK16, D) % W != 0) {
     return hipErrorInvalidValue;   // never chosen: choose_fwd_config skips it
   } else {
-  // 32-key steps use a ring of 4 buffers, 64-key steps a ring of 2
-  constexpr int NBUF = NK16 == 2 ? 4 : 2;
   auto kern = fwd_bf16_kernel<M16, W, NK16, NBUF, D>;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
@@ -494,10 +492,12 @@ hipError_t launch_one(const FwdParams &p, const FwdConfig &c, hipStream_t st) {
 // (rows per wave / 16, waves per workgroup) pairs built, in order of
 // preference; the first whose wave tile (16 * M16 rows) divides the frame
 // span wins.
-static const int kShapes[][2] = {{3, 4}, {2, 8}, {4, 4}, {2, 4}, {1, 4}, {3, 2}, {4, 2}, {2, 2}};
+static const int kShapes[][2] = {{2, 4}, {3, 4}, {1, 4}, {4, 4}, {2, 8}, {3, 2}, {4, 2}, {2, 2}};
 
-int fwd_bf16_lds_bytes(int nk16, int D) {
-  const int nbuf = nk16 == 2 ? 4 : 2;
+// (keys per step / 16, ring buffers) built; the first is the default.
+static const int kSteps[][2] = {{2, 2}, {2, 4}, {4, 2}};
+
+int fwd_bf16_lds_bytes(int nk16, int nbuf, int D) {
   return nbuf * 2 * (nk16 * 16) * (2 * D) + kMaxRuns * 8 + 16;
 }
 
@@ -509,44 +509,58 @@ bool choose_fwd_config(const fsattn_shape *s, const fsattn_mask *m, uint32_t fla
     cfg->waves = 1;
     cfg->m16 = R / 16;
     cfg->nk16 = 1;
+    cfg->nbuf = 1;
     cfg->lds_bytes = 2 * 16 * s->head_dim * 4 + kMaxRuns * 8 + 4;
     cfg->grid = (int64_t)m->num_frames * (T / R) * BH;
     return true;
   }
-  const int wo = (flags >> 8) & 15, mo = (flags >> 12) & 15, so = (flags >> 16) & 15;
-  const int nk16 = so ? so : 2;
-  if (nk16 != 2 && nk16 != 4) return false;
+  const int wo = (flags >> 8) & 15, mo = (flags >> 12) & 15, so = (flags >> 16) & 15,
+            bo = (flags >> 20) & 15;
+  int nk16 = 0, nbuf = 0;
+  for (const auto &st : kSteps)
+    if ((!so || st[0] == so) && (!bo || st[1] == bo)) {
+      nk16 = st[0];
+      nbuf = st[1];
+      break;
+    }
+  if (!nk16) return false;
   for (const auto &sh : kShapes) {
     const int m16 = sh[0], w = sh[1];
     if ((wo && w != wo) || (mo && m16 != mo)) continue;
     if (T % (16 * m16)) continue;
     if (copies_per_tile(nk16, s->head_dim) % w) continue;
+    // keep at least two workgroups per CU within the 160 KB of LDS
+    if (2 * fwd_bf16_lds_bytes(nk16, nbuf, s->head_dim) > 160 * 1024) continue;
     const int wave_tiles = T / (16 * m16);
     cfg->waves = w;
     cfg->m16 = m16;
     cfg->nk16 = nk16;
-    cfg->lds_bytes = fwd_bf16_lds_bytes(nk16, s->head_dim);
+    cfg->nbuf = nbuf;
+    cfg->lds_bytes = fwd_bf16_lds_bytes(nk16, nbuf, s->head_dim);
     cfg->grid = (int64_t)m->num_frames * ((wave_tiles + w - 1) / w) * BH;
     return true;
   }
   return false;
 }
 
+template <int M, int W, int D>
+hipError_t launch_steps(const FwdParams &p, const FwdConfig &c, hipStream_t st) {
+  if (c.nk16 == 2 && c.nbuf == 2) return launch_one<M, W, 2, 2, D>(p, c, st);
+  if (c.nk16 == 2 && c.nbuf == 4) return launch_one<M, W, 2, 4, D>(p, c, st);
+  if (c.nk16 == 4 && c.nbuf == 2) return launch_one<M, W, 4, 2, D>(p, c, st);
+  return hipErrorInvalidValue;
+}
+
 #define FSATTN_SHAPE_CASE(M, W)                                               \
-  if (c.m16 == M && c.waves == W) {                                           \
-    if (head_dim == 128)                                                      \
-      return c.nk16 == 4 ? launch_one<M, W, 4, 128>(p, c, st)                 \
-                         : launch_one<M, W, 2, 128>(p, c, st);                \
-    return c.nk16 == 4 ? launch_one<M, W, 4, 64>(p, c, st)                    \
-                       : launch_one<M, W, 2, 64>(p, c, st);                   \
-  }
+  if (c.m16 == M && c.waves == W)                                             \
+    return head_dim == 128 ? launch_steps<M, W, 128>(p, c, st) : launch_steps<M, W, 64>(p, c, st);
 
 hipError_t launch_forward_bf16(const FwdParams &p, const FwdConfig &c, int head_dim, hipStream_t st) {
-  FSATTN_SHAPE_CASE(3, 4)
-  FSATTN_SHAPE_CASE(2, 8)
-  FSATTN_SHAPE_CASE(4, 4)
   FSATTN_SHAPE_CASE(2, 4)
+  FSATTN_SHAPE_CASE(3, 4)
   FSATTN_SHAPE_CASE(1, 4)
+  FSATTN_SHAPE_CASE(4, 4)
+  FSATTN_SHAPE_CASE(2, 8)
   FSATTN_SHAPE_CASE(3, 2)
   FSATTN_SHAPE_CASE(4, 2)
   FSATTN_SHAPE_CASE(2, 2)

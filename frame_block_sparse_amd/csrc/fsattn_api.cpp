@@ -118,7 +118,7 @@ extern "C" fsattn_status fsattn_head_bounds(void *hip_stream, const fsattn_shape
 
 namespace {
 
-constexpr uint32_t kKnownFlags = 0x7u | (0xfu << 8) | (0xfu << 12) | (0xfu << 16);
+constexpr uint32_t kKnownFlags = 0x7u | (0xfu << 8) | (0xfu << 12) | (0xfu << 16) | (0xfu << 20);
 
 fsattn_status check_forward_host(const fsattn_shape *s, const fsattn_mask *m, uint32_t flags, FwdConfig *cfg) {
   fsattn_status st = check_shape(s, m);

@@ -57,7 +57,7 @@ struct FwdParams {
 constexpr int kMaxOrderedFrames = 64;
 
 struct FwdConfig {
-  int waves, m16, nk16;   // waves per workgroup, rows per wave / 16, keys per step / 16
+  int waves, m16, nk16, nbuf;   // waves per workgroup, rows per wave / 16, keys per step / 16, ring buffers
   int lds_bytes;
   int64_t grid;
 };

@@ -236,13 +236,14 @@ _MODES = {"auto": MODE_AUTO, "online": MODE_FORCE_ONLINE, "fixed": MODE_FORCE_FI
 
 
 def make_flags(mode: str = "auto", per_row_shift: bool = False, waves: int = 0, rows_per_wave: int = 0,
-               key_step: int = 0) -> int:
+               key_step: int = 0, ring: int = 0) -> int:
     f = _MODES[mode]
     if per_row_shift:
         f |= SHIFT_PER_ROW
     f |= (waves & 15) << 8
     f |= ((rows_per_wave // 16) & 15) << 12
     f |= ((key_step // 16) & 15) << 16
+    f |= (ring & 15) << 20
     return f
 
 

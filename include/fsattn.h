@@ -121,14 +121,17 @@ enum {
   FSATTN_SHIFT_PER_ROW = 4       /* fixed shift scale*(|q_i|*k_norm_max + q_i.mu)
                                     instead of bound + scale*q_i.mu */
 };
-/* Optional launch-shape overrides in the flags word (0 = library choice):
- * bits 8..11 waves per workgroup (1..8), bits 12..15 query rows per wave
- * divided by 16 (2..5), bits 16..19 keys per pipeline step divided by 16
- * (2 or 4). An override that does not fit the geometry returns
+/* Optional launch-shape overrides in the flags word (0 = library choice),
+ * bf16 inputs only: bits 8..11 waves per workgroup (1, 2, 4 or 8), bits
+ * 12..15 query rows per wave divided by 16 (1..4; must divide
+ * tokens_per_frame / 16), bits 16..19 keys per pipeline step divided by 16
+ * (2 or 4), bits 20..23 K/V staging buffers in the ring (2 or 4). An
+ * override that is not built or does not fit the geometry returns
  * FSATTN_ERR_UNSUPPORTED. */
 #define FSATTN_FLAG_WAVES(n) ((uint32_t)(n) << 8)
 #define FSATTN_FLAG_ROWS16(m) ((uint32_t)(m) << 12)
 #define FSATTN_FLAG_KSTEP16(s) ((uint32_t)(s) << 16)
+#define FSATTN_FLAG_RING(b) ((uint32_t)(b) << 20)
 
 #define FSATTN_DEFAULT_GAP_NATS 30.0f
 

@@ -114,8 +114,8 @@ SMALL = [
 ]
 
 # (waves, rows per wave) of every built launch shape, and the key steps
-SHAPES = [(4, 48), (8, 32), (4, 64), (4, 32), (4, 16), (2, 48), (2, 64), (2, 32)]
-SHAPE_OVERRIDES = [(w, r, ks) for (w, r) in SHAPES for ks in (32, 64)]
+SHAPES = [(4, 32), (4, 48), (4, 16), (4, 64), (8, 32), (2, 48), (2, 64), (2, 32)]
+SHAPE_OVERRIDES = [(w, r, ks, rb) for (w, r) in SHAPES for (ks, rb) in ((32, 2), (32, 4), (64, 2))]
 
 
 def _small(case, seed=0, key_offset=0.0):
@@ -145,20 +145,20 @@ def test_forward_small_parity(dev, case, mode):
 _SHAPE_REF = {}
 
 
-@pytest.mark.parametrize("shape", SHAPE_OVERRIDES, ids=[f"w{a}_r{b}_k{c}" for a, b, c in SHAPE_OVERRIDES])
+@pytest.mark.parametrize("shape", SHAPE_OVERRIDES, ids=[f"w{a}_r{b}_k{c}_b{d}" for a, b, c, d in SHAPE_OVERRIDES])
 def test_forward_launch_shapes(dev, shape):
     """Every built launch shape on a frame span its wave tile divides; several
     leave the frame's last workgroup ragged (idle waves)."""
-    waves, rows, kstep = shape
+    waves, rows, kstep, ring = shape
     T = next(t for t in (720, 960, 768) if t % rows == 0)
     case = (f"shapes{T}", 1, 2, 3, T, 128, "bf16", 1, 1, 0, 48, 48)
     w, q, k, v = _small(case, seed=2)
     if T not in _SHAPE_REF:
         _SHAPE_REF[T] = oracle.attention_ref(q, k, v, _geom(w))[0]
     ref = _SHAPE_REF[T]
-    _say(f"[fwd-shape] T={T} waves={waves} rows={rows} kstep={kstep}")
+    _say(f"[fwd-shape] T={T} waves={waves} rows={rows} kstep={kstep} ring={ring}")
     for mode in ("auto", "online"):
-        flags = fs.make_flags(mode, waves=waves, rows_per_wave=rows, key_step=kstep)
+        flags = fs.make_flags(mode, waves=waves, rows_per_wave=rows, key_step=kstep, ring=ring)
         assert fs.launch_info((1, 2, 3 * T, 128), fs.BF16, w, flags)[:3] == (waves, rows, kstep)
         out, _, _ = _run(w, q, k, v, dev, flags=flags)
         err = np.abs(out.float().cpu().numpy() - ref).max()
