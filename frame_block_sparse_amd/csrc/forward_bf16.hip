@@ -158,6 +158,9 @@ void fwd_bf16_kernel(FwdParams p) {
   constexpr int RPI = 1024 / ROWB;    // rows written by one wave-wide 16-byte load
   constexpr int NI = NK / RPI;        // such loads per tile
   constexpr int CPR = D / 8;          // 16-byte chunks per row
+  // Register prefetch of K and V fragments (below) fits the register budget
+  // of 32-key steps with at least 4 waves; the other shapes spill with it.
+  constexpr bool PF = NK16 == 2 && W >= 4;
   // swizzles: K chunk c of row r lives at chunk c ^ ksw(r); V 32-byte
   // segment s of row r lives at segment s ^ vsw(r). Rows are 256 bytes for
   // d = 128 (one full bank row), 128 bytes for d = 64 (two rows per bank row).
@@ -305,15 +308,42 @@ void fwd_bf16_kernel(FwdParams p) {
     for (int m = 0; m < M16; ++m)
 #pragma unroll
       for (int t = 0; t < NS; ++t) s[m][t] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kd = 0; kd < KD; ++kd)
+    // With prefetch the K fragments are double-buffered in registers: the
+    // reads for slice kd+1 are in flight while the MFMAs of slice kd issue
+    // (scheduling fences keep the compiler from sinking them next to their
+    // use).
+    constexpr int KB = PF && NS == 2 ? 2 : 1;
+    [[maybe_unused]] bf16x8 ka[KB][NS];
+    auto kload = [&](int kd, int slot) {
 #pragma unroll
       for (int t = 0; t < NS; ++t) {
         const int r = key0 + 16 * t + n16;
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kt + r * ROWB + 16 * ((4 * kd + g) ^ ksw(r)));
-#pragma unroll
-        for (int m = 0; m < M16; ++m) s[m][t] = mfma32(a, qf[m][kd], s[m][t]);
+        ka[slot][t] = *reinterpret_cast<const bf16x8 *>(kt + r * ROWB + 16 * ((4 * kd + g) ^ ksw(r)));
       }
+    };
+    if constexpr (KB == 2) {
+      kload(0, 0);
+#pragma unroll
+      for (int kd = 0; kd < KD; ++kd) {
+        if (kd + 1 < KD) kload(kd + 1, (kd + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < NS; ++t)
+#pragma unroll
+          for (int m = 0; m < M16; ++m) s[m][t] = mfma32(ka[kd & 1][t], qf[m][kd], s[m][t]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int kd = 0; kd < KD; ++kd)
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+          const int r = key0 + 16 * t + n16;
+          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kt + r * ROWB + 16 * ((4 * kd + g) ^ ksw(r)));
+#pragma unroll
+          for (int m = 0; m < M16; ++m) s[m][t] = mfma32(a, qf[m][kd], s[m][t]);
+        }
+    }
     if constexpr (!FIXED) {
       // Online softmax: raise the running max where a row's chunk maximum
       // exceeds it; rescale only when some row of the wave changed.
@@ -342,6 +372,35 @@ void fwd_bf16_kernel(FwdParams p) {
         }
       }
     }
+    // V rows of this lane's transposed reads: vr (keys 4g..4g+3 of the first
+    // 16-key tile) and vr + 16; after the swizzle a row's 32-byte segment for
+    // output tile dt sits at byte 32 * (dt ^ vsw(row)). With prefetch the
+    // first VF-1 fragments are requested before the exponentials so that
+    // their latency hides behind them; each PV step then requests fragment
+    // dt+VF-1.
+    constexpr int VF = 3;
+    constexpr bool VPF = PF && NS == 2;
+    struct VAddr {
+      const unsigned char *v0, *v1;
+      int sw;
+    };
+    auto vaddr = [&]() {
+      const int vr = key0 + 4 * g + (n16 >> 2);
+      const unsigned char *v0 = vt + vr * ROWB + 8 * (n16 & 3);
+      return VAddr{v0, v0 + 16 * ROWB, vsw(vr)};   // vsw(vr + 16) == vsw(vr)
+    };
+    bf16x4 va[VF][2];
+    [[maybe_unused]] VAddr pa;
+    if constexpr (VPF) {
+      pa = vaddr();
+      const unsigned char *v0 = pa.v0, *v1 = pa.v1;
+      const int sw = pa.sw;
+#pragma unroll
+      for (int j = 0; j < VF - 1; ++j) {
+        va[j][0] = lds_read_tr(v0 + 32 * (j ^ sw));
+        va[j][1] = lds_read_tr(v1 + 32 * (j ^ sw));
+      }
+    }
     bf16x8 pk[M16];
     bf16x4 pt[M16];
 #pragma unroll
@@ -366,25 +425,38 @@ void fwd_bf16_kernel(FwdParams p) {
         for (int i = 0; i < 4; ++i) pt[m][i] = (__bf16)s[m][0][i];
       }
     }
-    // V rows of this lane's transposed reads: vr (keys 4g..4g+3 of the first
-    // 16-key tile) and vr + 16; after the swizzle a row's 32-byte segment for
-    // output tile dt sits at byte 32 * (dt ^ vsw(row)).
-    const int vr = key0 + 4 * g + (n16 >> 2);
-    const unsigned char *v0 = vt + vr * ROWB + 8 * (n16 & 3);
-    const unsigned char *v1 = v0 + 16 * ROWB;
-    const int sw = vsw(vr);   // vsw(vr + 16) == vsw(vr)
+    if constexpr (VPF) {
+      const unsigned char *v0 = pa.v0, *v1 = pa.v1;
+      const int sw = pa.sw;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      if constexpr (NS == 2) {
-        const bf16x4 lo = lds_read_tr(v0 + 32 * (dt ^ sw));
-        const bf16x4 hi = lds_read_tr(v1 + 32 * (dt ^ sw));
-        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      for (int dt = 0; dt < DT; ++dt) {
+        if (dt + VF - 1 < DT) {
+          va[(dt + VF - 1) % VF][0] = lds_read_tr(v0 + 32 * ((dt + VF - 1) ^ sw));
+          va[(dt + VF - 1) % VF][1] = lds_read_tr(v1 + 32 * ((dt + VF - 1) ^ sw));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 a = __builtin_shufflevector(va[dt % VF][0], va[dt % VF][1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int m = 0; m < M16; ++m) oacc[m][dt] = mfma32(a, pk[m], oacc[m][dt]);
-      } else {
-        const bf16x4 a = lds_read_tr(v0 + 32 * (dt ^ sw));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      const VAddr a0 = vaddr();
+      const unsigned char *v0 = a0.v0, *v1 = a0.v1;
+      const int sw = a0.sw;
 #pragma unroll
-        for (int m = 0; m < M16; ++m) oacc[m][dt] = mfma16(a, pt[m], oacc[m][dt]);
+      for (int dt = 0; dt < DT; ++dt) {
+        if constexpr (NS == 2) {
+          const bf16x4 lo = lds_read_tr(v0 + 32 * (dt ^ sw));
+          const bf16x4 hi = lds_read_tr(v1 + 32 * (dt ^ sw));
+          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+          for (int m = 0; m < M16; ++m) oacc[m][dt] = mfma32(a, pk[m], oacc[m][dt]);
+        } else {
+          const bf16x4 a = lds_read_tr(v0 + 32 * (dt ^ sw));
+#pragma unroll
+          for (int m = 0; m < M16; ++m) oacc[m][dt] = mfma16(a, pt[m], oacc[m][dt]);
+        }
       }
     }
   };
