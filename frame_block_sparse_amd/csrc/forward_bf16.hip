@@ -281,20 +281,40 @@ void fwd_bf16_kernel(FwdParams p) {
   // Byte offsets within a step are 32-bit (the host guarantees that 64 rows
   // of either tensor span less than 2^31 bytes).
   const unsigned kstride2 = (unsigned)(2 * p.ksn), vstride2 = (unsigned)(2 * p.vsn);
-  const unsigned lds_base = (unsigned)(uintptr_t)(lds_uchar *)smem;
+  const unsigned lds_base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_uchar *)smem);
+  auto src_off = [&](int j, int kl, unsigned &ko, unsigned &vo) {
+    const int r = RPI * (wave + j * W) + lrow;
+    const unsigned rs = (unsigned)min(r, kl - 1);
+    const unsigned ck = lchunk ^ ksw(r);
+    const unsigned cv = (((lchunk >> 1) ^ vsw(r)) << 1) | (lchunk & 1);
+    ko = rs * kstride2 + 16u * ck;
+    vo = rs * vstride2 + 16u * cv;
+  };
+  // A wave's successive copies are RPI * W rows apart. When that is a
+  // multiple of 16 (the period of both swizzles), every copy of a full step
+  // reads the same chunk of its row, so a lane's offset is one fixed value
+  // per tensor and the copy's row distance goes into the wave-uniform base.
+  constexpr int JROWS = RPI * W;
+  constexpr bool JINV = JROWS % 16 == 0;
+  unsigned koff0 = 0, voff0 = 0;
+  if constexpr (JINV) src_off(0, NK, koff0, voff0);
   auto issue_loads = [&](int buf, int ks0, int kl) {
-    const uint64_t ksrc = uniform_ptr(kb + (int64_t)ks0 * p.ksn);
-    const uint64_t vsrc = uniform_ptr(vb + (int64_t)ks0 * p.vsn);
+    const __bf16 *kr = kb + (int64_t)ks0 * p.ksn;
+    const __bf16 *vr = vb + (int64_t)ks0 * p.vsn;
     const unsigned kdst = lds_base + 2 * buf * TILEB;
+    const bool fast = JINV && kl == NK;   // wave-uniform
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
-      const int r = RPI * (wave + j * W) + lrow;
-      const unsigned rs = (unsigned)min(r, kl - 1);
-      const unsigned ck = lchunk ^ ksw(r);
-      const unsigned cv = (((lchunk >> 1) ^ vsw(r)) << 1) | (lchunk & 1);
       const unsigned row0b = (unsigned)(RPI * (wave + j * W) * ROWB);
-      dma16(ksrc, rs * kstride2 + 16u * ck, __builtin_amdgcn_readfirstlane(kdst + row0b));
-      dma16(vsrc, rs * vstride2 + 16u * cv, __builtin_amdgcn_readfirstlane(kdst + TILEB + row0b));
+      if (fast) {
+        dma16(uniform_ptr(kr + (int64_t)(j * JROWS) * p.ksn), koff0, kdst + row0b);
+        dma16(uniform_ptr(vr + (int64_t)(j * JROWS) * p.vsn), voff0, kdst + TILEB + row0b);
+      } else {
+        unsigned ko, vo;
+        src_off(j, kl, ko, vo);
+        dma16(uniform_ptr(kr), ko, kdst + row0b);
+        dma16(uniform_ptr(vr), vo, kdst + TILEB + row0b);
+      }
     }
   };
 
@@ -567,7 +587,7 @@ hipError_t launch_one(const FwdParams &p, const FwdConfig &c, hipStream_t st) {
 static const int kShapes[][2] = {{2, 4}, {3, 4}, {1, 4}, {4, 4}, {2, 8}, {3, 2}, {4, 2}, {2, 2}};
 
 // (keys per step / 16, ring buffers) built; the first is the default.
-static const int kSteps[][2] = {{2, 2}, {2, 4}, {4, 2}};
+static const int kSteps[][2] = {{2, 2}, {2, 3}, {2, 4}, {4, 2}};
 
 int fwd_bf16_lds_bytes(int nk16, int nbuf, int D) {
   return nbuf * 2 * (nk16 * 16) * (2 * D) + kMaxRuns * 8 + 16;
@@ -618,6 +638,7 @@ bool choose_fwd_config(const fsattn_shape *s, const fsattn_mask *m, uint32_t fla
 template <int M, int W, int D>
 hipError_t launch_steps(const FwdParams &p, const FwdConfig &c, hipStream_t st) {
   if (c.nk16 == 2 && c.nbuf == 2) return launch_one<M, W, 2, 2, D>(p, c, st);
+  if (c.nk16 == 2 && c.nbuf == 3) return launch_one<M, W, 2, 3, D>(p, c, st);
   if (c.nk16 == 2 && c.nbuf == 4) return launch_one<M, W, 2, 4, D>(p, c, st);
   if (c.nk16 == 4 && c.nbuf == 2) return launch_one<M, W, 4, 2, D>(p, c, st);
   return hipErrorInvalidValue;

@@ -169,6 +169,14 @@ def test_launch_info_choices():
     assert (waves, rows) == (2, 48)
     with pytest.raises(fs.FsattnError):           # 5-wave workgroups are not built
         fs.launch_info((1, 5, 32400, 128), fs.BF16, w, fs.make_flags(waves=5, rows_per_wave=48))
+    w2 = workloads.config(2)
+    shape2 = (w2.batch, w2.heads, w2.seq_len, w2.head_dim)
+    for ring, kstep, lds_expect in ((2, 32, 2 * 2 * 32 * 256), (3, 32, 3 * 2 * 32 * 256),
+                                    (4, 32, 4 * 2 * 32 * 256), (2, 64, 2 * 2 * 64 * 256)):
+        _, _, ks, _, lds = fs.launch_info(shape2, fs.BF16, w2, fs.make_flags(key_step=kstep, ring=ring))
+        assert ks == kstep and lds_expect <= lds < lds_expect + 1024
+    with pytest.raises(fs.FsattnError):           # a 3-buffer ring of 64-key steps is not built
+        fs.launch_info(shape2, fs.BF16, w2, fs.make_flags(key_step=64, ring=3))
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

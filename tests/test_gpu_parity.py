@@ -115,7 +115,7 @@ SMALL = [
 
 # (waves, rows per wave) of every built launch shape, and the key steps
 SHAPES = [(4, 32), (4, 48), (4, 16), (4, 64), (8, 32), (2, 48), (2, 64), (2, 32)]
-SHAPE_OVERRIDES = [(w, r, ks, rb) for (w, r) in SHAPES for (ks, rb) in ((32, 2), (32, 4), (64, 2))]
+SHAPE_OVERRIDES = [(w, r, ks, rb) for (w, r) in SHAPES for (ks, rb) in ((32, 2), (32, 3), (32, 4), (64, 2))]
 
 
 def _small(case, seed=0, key_offset=0.0):
