@@ -60,6 +60,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned u4 __attribute__((ext_vector_type(4)));
+typedef unsigned u2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) short4v lds_short4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) unsigned char lds_uchar;
@@ -81,6 +84,12 @@ __device__ inline bf16x4 lds_read_tr(const unsigned char *p) {
   return __builtin_bit_cast(bf16x4, r);
 }
 
+// acc + x.lo + x.hi for a packed bf16 pair (v_dot2c_f32_bf16 with (1, 1)).
+__device__ inline float add_bf16_pair(float acc, unsigned x) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), one, acc, false);
+}
+
 // One wave-wide global -> LDS copy of 16 bytes per lane
 // (global_load_lds_dwordx4): lane l's bytes land at LDS address lds + 16*l.
 // Issued from inline assembly so that the compiler's wait insertion, which
@@ -90,14 +99,18 @@ __device__ inline bf16x4 lds_read_tr(const unsigned char *p) {
 // other code in these kernels uses M0.
 // The address is a wave-uniform 64-bit base (SGPR pair) plus a 32-bit
 // per-lane byte offset.
-__device__ inline void dma16(uint64_t base, unsigned off, unsigned lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory");
-}
-__device__ inline uint64_t uniform_ptr(const void *p) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
+__device__ inline uint64_t uniform_u64(uint64_t a) {
   const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
   const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
   return ((uint64_t)hi << 32) | lo;
+}
+__device__ inline uint64_t uniform_ptr(const void *p) { return uniform_u64(reinterpret_cast<uint64_t>(p)); }
+// (the scalar operands pass through readfirstlane, which only states what
+// they already are: wave-uniform)
+__device__ inline void dma16(uint64_t base, unsigned off, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(uniform_u64(base)),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
 }
 
 // s_waitcnt vmcnt(0) through the builtin, which the compiler's own wait
@@ -186,8 +199,10 @@ void fwd_bf16_kernel(FwdParams p) {
   if (wave == 0) build_runs(p.row_ptr, p.col_idx, p.nnz, row0 / p.bq, p.bk, p.N, runs, nruns_sm);
 
   const __bf16 *qb = static_cast<const __bf16 *>(p.q) + b * p.qsb + h * p.qsh;
-  const __bf16 *kb = static_cast<const __bf16 *>(p.k) + b * p.ksb + h * p.ksh;
-  const __bf16 *vb = static_cast<const __bf16 *>(p.v) + b * p.vsb + h * p.vsh;
+  // K and V bases of this (batch, head) as wave-uniform byte addresses: the
+  // copies' addresses are computed on the scalar unit
+  const uint64_t kb = uniform_ptr(static_cast<const __bf16 *>(p.k) + b * p.ksb + h * p.ksh);
+  const uint64_t vb = uniform_ptr(static_cast<const __bf16 *>(p.v) + b * p.vsb + h * p.vsh);
   const int wrow0 = row0 + wave * 16 * M16;
 
   // Q fragments (B operand of S^T = K Q^T): row n16 of each 16-row group,
@@ -245,26 +260,31 @@ void fwd_bf16_kernel(FwdParams p) {
   const float c2 = p.scale_log2;
 
   __syncthreads();
-  const int nr = *nruns_sm;
-  // Step iterator over the runs: next step's first key and length. Each
-  // iterator keeps its current run's bounds in scalar registers and reads
-  // the run table only when it moves to the next run. The loads run
-  // NBUF-1 steps ahead of the compute, each with its own iterator.
+  // The frame mask gives every query frame at most two runs of live keys
+  // (the window, and the reference frame when it is not adjacent to it);
+  // the host rejects masks with more. Their bounds live in scalar registers.
+  const int nr = min(*nruns_sm, 2);
+  const int r0s = nr > 0 ? __builtin_amdgcn_readfirstlane(runs[0].x) : 0;
+  const int r0e = nr > 0 ? __builtin_amdgcn_readfirstlane(runs[0].y) : 0;
+  const int r1s = nr > 1 ? __builtin_amdgcn_readfirstlane(runs[1].x) : 0;
+  const int r1e = nr > 1 ? __builtin_amdgcn_readfirstlane(runs[1].y) : 0;
+  // Step iterator over the two runs: next step's length.
   struct Iter {
-    int ri, pos, end;
+    int pos, end;
+    bool second;
   };
   auto iter_init = [&](Iter &it) {
-    it.ri = 0;
-    it.pos = nr > 0 ? __builtin_amdgcn_readfirstlane(runs[0].x) : 0;
-    it.end = nr > 0 ? __builtin_amdgcn_readfirstlane(runs[0].y) : 0;
+    it.pos = r0s;
+    it.end = r0e;
+    it.second = false;
   };
-  auto next_step = [&](Iter &it, int &ks0, int &kl) -> bool {
-    while (it.pos >= it.end) {
-      if (++it.ri >= nr) return false;
-      it.pos = __builtin_amdgcn_readfirstlane(runs[it.ri].x);
-      it.end = __builtin_amdgcn_readfirstlane(runs[it.ri].y);
+  auto next_step = [&](Iter &it, int &kl) -> bool {
+    if (it.pos >= it.end) {
+      if (it.second || r1s >= r1e) return false;
+      it.pos = r1s;
+      it.end = r1e;
+      it.second = true;
     }
-    ks0 = it.pos;
     kl = min(NK, it.end - it.pos);
     it.pos += kl;
     return true;
@@ -298,22 +318,50 @@ void fwd_bf16_kernel(FwdParams p) {
   constexpr bool JINV = JROWS % 16 == 0;
   unsigned koff0 = 0, voff0 = 0;
   if constexpr (JINV) src_off(0, NK, koff0, voff0);
-  auto issue_loads = [&](int buf, int ks0, int kl) {
-    const __bf16 *kr = kb + (int64_t)ks0 * p.ksn;
-    const __bf16 *vr = vb + (int64_t)ks0 * p.vsn;
+  // The load-side iterator also carries the byte addresses of its step's
+  // first K and V rows, advanced by a constant per full step and set once
+  // per run.
+  const uint64_t kstep = 2 * (uint64_t)p.ksn, vstep = 2 * (uint64_t)p.vsn;   // bytes per row
+  struct LIter {
+    Iter it;
+    uint64_t kr, vr;
+  };
+  auto liter_init = [&](LIter &L) {
+    iter_init(L.it);
+    L.kr = kb + (uint64_t)r0s * kstep;
+    L.vr = vb + (uint64_t)r0s * vstep;
+  };
+  auto lnext = [&](LIter &L, int &kl, uint64_t &kr, uint64_t &vr) -> bool {
+    if (L.it.pos >= L.it.end) {
+      if (L.it.second || r1s >= r1e) return false;
+      L.it.pos = r1s;
+      L.it.end = r1e;
+      L.it.second = true;
+      L.kr = kb + (uint64_t)r1s * kstep;
+      L.vr = vb + (uint64_t)r1s * vstep;
+    }
+    kl = min(NK, L.it.end - L.it.pos);
+    kr = L.kr;
+    vr = L.vr;
+    L.it.pos += kl;
+    L.kr += NK * kstep;   // a short step ends its run, so this is not used
+    L.vr += NK * vstep;
+    return true;
+  };
+  auto issue_loads = [&](int buf, uint64_t kr, uint64_t vr, int kl) {
     const unsigned kdst = lds_base + 2 * buf * TILEB;
     const bool fast = JINV && kl == NK;   // wave-uniform
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       const unsigned row0b = (unsigned)(RPI * (wave + j * W) * ROWB);
       if (fast) {
-        dma16(uniform_ptr(kr + (int64_t)(j * JROWS) * p.ksn), koff0, kdst + row0b);
-        dma16(uniform_ptr(vr + (int64_t)(j * JROWS) * p.vsn), voff0, kdst + TILEB + row0b);
+        dma16(kr + (uint64_t)(j * JROWS) * kstep, koff0, kdst + row0b);
+        dma16(vr + (uint64_t)(j * JROWS) * vstep, voff0, kdst + TILEB + row0b);
       } else {
         unsigned ko, vo;
         src_off(j, kl, ko, vo);
-        dma16(uniform_ptr(kr), ko, kdst + row0b);
-        dma16(uniform_ptr(vr), vo, kdst + TILEB + row0b);
+        dma16(kr, ko, kdst + row0b);
+        dma16(vr, vo, kdst + TILEB + row0b);
       }
     }
   };
@@ -429,20 +477,24 @@ void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int t = 0; t < NS; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(s[m][t][i], c2, nsh));
-          lsum[m] += e;
-          s[m][t][i] = e;
-        }
+        for (int i = 0; i < 4; ++i) s[m][t][i] = __builtin_amdgcn_exp2f(fmaf(s[m][t][i], c2, nsh));
+      // the row sum adds the probabilities PV multiplies (bf16), a pair per
+      // v_dot2c_f32_bf16
       if constexpr (NS == 2) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           pk[m][i] = (__bf16)s[m][0][i];
           pk[m][4 + i] = (__bf16)s[m][1][i];
         }
+        const u4 w = __builtin_bit_cast(u4, pk[m]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lsum[m] = add_bf16_pair(lsum[m], w[j]);
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) pt[m][i] = (__bf16)s[m][0][i];
+        const u2 w = __builtin_bit_cast(u2, pt[m]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) lsum[m] = add_bf16_pair(lsum[m], w[j]);
       }
     }
     if constexpr (VPF) {
@@ -483,20 +535,22 @@ void fwd_bf16_kernel(FwdParams p) {
   // The step loop, instantiated once per softmax path so that the two
   // paths never merge inside it.
   auto main_loop = [&](auto fixed_tag) {
-    Iter li, ci;
-    iter_init(li);
+    LIter li;
+    Iter ci;
+    liter_init(li);
     iter_init(ci);
     int issued = 0;
 #pragma unroll
     for (int j = 0; j < NBUF - 1; ++j) {
-      int ks = 0, kl = 0;
-      if (next_step(li, ks, kl)) {
-        issue_loads(j, ks, kl);
+      int kl = 0;
+      uint64_t kr = 0, vr = 0;
+      if (lnext(li, kl, kr, vr)) {
+        issue_loads(j, kr, vr, kl);
         ++issued;
       }
     }
-    int step = 0, cks = 0, ckl = 0;
-    while (next_step(ci, cks, ckl)) {
+    int step = 0, ckl = 0;
+    while (next_step(ci, ckl)) {
       // my copies of this step are done once at most (issued - step - 1)
       // later steps' copies are outstanding
       const int later = issued - step - 1;
@@ -506,9 +560,10 @@ void fwd_bf16_kernel(FwdParams p) {
       else wait_vmem();
       __syncthreads();   // every wave's copies of this step landed; step-1 is free
       {
-        int ks = 0, kl = 0;
-        if (next_step(li, ks, kl)) {
-          issue_loads((step + NBUF - 1) % NBUF, ks, kl);
+        int kl = 0;
+        uint64_t kr = 0, vr = 0;
+        if (lnext(li, kl, kr, vr)) {
+          issue_loads((step + NBUF - 1) % NBUF, kr, vr, kl);
           ++issued;
         }
       }

@@ -125,7 +125,9 @@ fsattn_status check_forward_host(const fsattn_shape *s, const fsattn_mask *m, ui
   if (st != FSATTN_OK) return st;
   if (flags & ~kKnownFlags) return FSATTN_ERR_INVALID_ARGUMENT;
   if ((flags & 3) == 3) return FSATTN_ERR_INVALID_ARGUMENT;
-  if (max_runs_per_frame(m) > kMaxRuns) return FSATTN_ERR_UNSUPPORTED;
+  // the bf16 kernel walks at most two key runs per query frame (window and
+  // reference frame), which is all this mask family produces
+  if (max_runs_per_frame(m) > (s->dtype == FSATTN_BF16 ? 2 : kMaxRuns)) return FSATTN_ERR_UNSUPPORTED;
   if (s->dtype == FSATTN_F32 && (flags & (0xfffu << 8))) return FSATTN_ERR_UNSUPPORTED;
   if (!choose_fwd_config(s, m, flags, cfg)) return FSATTN_ERR_UNSUPPORTED;
   if (cfg->grid / ((int64_t)s->batch * s->heads) > INT32_MAX) return FSATTN_ERR_UNSUPPORTED;

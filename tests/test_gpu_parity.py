@@ -18,6 +18,12 @@ import workloads
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-5, "bf16": 2e-2}
+# Log-sum-exp bound.  The bf16 kernel sums the probabilities after rounding them
+# to bf16 (the same weights the PV product multiplies, so the output stays a
+# convex combination of value rows).  Each weight then carries a relative error
+# of at most 2^-9, so the sum does too, and the log of the sum moves by at most
+# log1p(2^-9) < 1.96e-3; the fp32 accumulation adds far less.
+LSE_TOL = {"f32": 1e-5, "bf16": 2.5e-3}
 
 
 def _say(msg):
@@ -139,7 +145,7 @@ def test_forward_small_parity(dev, case, mode):
     err = np.abs(out.float().cpu().numpy() - ref).max()
     assert err <= TOL[w.dtype], err
     lerr = np.abs(lse.cpu().numpy() - ref_lse).max()
-    assert lerr <= (1e-5 if w.dtype == "f32" else 1e-3), lerr
+    assert lerr <= LSE_TOL[w.dtype], lerr
 
 
 _SHAPE_REF = {}
