@@ -64,6 +64,7 @@ typedef unsigned u4 __attribute__((ext_vector_type(4)));
 typedef unsigned u2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) short4v lds_short4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) unsigned char lds_uchar;
 typedef __attribute__((address_space(1))) void glb_void;
@@ -79,10 +80,12 @@ __device__ inline f4 mfma16(bf16x4 a, bf16x4 b, f4 c) {
 // Transposed LDS read: the 16 lanes of a group address a 4 x 16 block
 // (row j/4, columns 4*(j%4)..+3 for lane j); lane i receives column i of
 // the four rows.
-__device__ inline bf16x4 lds_read_tr(const unsigned char *p) {
-  const short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)((lds_uchar *)p));
+__device__ inline bf16x4 lds_read_tr(unsigned addr) {
+  const short4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(uintptr_t)addr);
   return __builtin_bit_cast(bf16x4, r);
 }
+// 16-byte LDS read at an LDS byte address.
+__device__ inline bf16x8 lds_read16(unsigned addr) { return *(const lds_bf16x8 *)(uintptr_t)addr; }
 
 // acc + x.lo + x.hi for a packed bf16 pair (v_dot2c_f32_bf16 with (1, 1)).
 __device__ inline float add_bf16_pair(float acc, unsigned x) {
@@ -268,27 +271,19 @@ void fwd_bf16_kernel(FwdParams p) {
   const int r0e = nr > 0 ? __builtin_amdgcn_readfirstlane(runs[0].y) : 0;
   const int r1s = nr > 1 ? __builtin_amdgcn_readfirstlane(runs[1].x) : 0;
   const int r1e = nr > 1 ? __builtin_amdgcn_readfirstlane(runs[1].y) : 0;
-  // Step iterator over the two runs: next step's length.
-  struct Iter {
-    int pos, end;
-    bool second;
-  };
-  auto iter_init = [&](Iter &it) {
-    it.pos = r0s;
-    it.end = r0e;
-    it.second = false;
-  };
-  auto next_step = [&](Iter &it, int &kl) -> bool {
-    if (it.pos >= it.end) {
-      if (it.second || r1s >= r1e) return false;
-      it.pos = r1s;
-      it.end = r1e;
-      it.second = true;
-    }
-    kl = min(NK, it.end - it.pos);
-    it.pos += kl;
-    return true;
-  };
+  // Steps: first the F0 full NK-key steps of run 0 and the F1 of run 1,
+  // then the short remainder of each run that has one (16 * k keys, k < NK
+  // / 16): the order of the keys does not change the result, and the loop
+  // over full steps then has no length test.
+  const int len0 = r0e - r0s, len1 = r1e - r1s;
+  const int F0 = len0 / NK, F1 = len1 / NK;
+  const int nfull = F0 + F1;
+  const int t0 = len0 - NK * F0, t1 = len1 - NK * F1;   // remainders
+  const int nsteps = nfull + (t0 > 0) + (t1 > 0);
+  // remainder step nfull + e: its run's first remainder row, end and length
+  const int tpos0 = t0 > 0 ? r0s + NK * F0 : r1s + NK * F1, tend0 = t0 > 0 ? r0e : r1e;
+  const int tlen0 = t0 > 0 ? t0 : t1;
+  const int tpos1 = r1s + NK * F1, tend1 = r1e, tlen1 = t1;
 
   // Global -> LDS copies. A tile of NK rows is NI wave-wide copies of RPI
   // rows; wave w issues copies w, w + W, ... of K, then the same of V
@@ -318,39 +313,25 @@ void fwd_bf16_kernel(FwdParams p) {
   constexpr bool JINV = JROWS % 16 == 0;
   unsigned koff0 = 0, voff0 = 0;
   if constexpr (JINV) src_off(0, NK, koff0, voff0);
-  // The load-side iterator also carries the byte addresses of its step's
-  // first K and V rows, advanced by a constant per full step and set once
-  // per run.
+  // The copy side walks the steps in order with the byte addresses of its
+  // next step's first K and V rows, advanced by one step's stride and set
+  // to run 1's first row when it gets there.
   const uint64_t kstep = 2 * (uint64_t)p.ksn, vstep = 2 * (uint64_t)p.vsn;   // bytes per row
-  struct LIter {
-    Iter it;
-    uint64_t kr, vr;
-  };
-  auto liter_init = [&](LIter &L) {
-    iter_init(L.it);
-    L.kr = kb + (uint64_t)r0s * kstep;
-    L.vr = vb + (uint64_t)r0s * vstep;
-  };
-  auto lnext = [&](LIter &L, int &kl, uint64_t &kr, uint64_t &vr) -> bool {
-    if (L.it.pos >= L.it.end) {
-      if (L.it.second || r1s >= r1e) return false;
-      L.it.pos = r1s;
-      L.it.end = r1e;
-      L.it.second = true;
-      L.kr = kb + (uint64_t)r1s * kstep;
-      L.vr = vb + (uint64_t)r1s * vstep;
-    }
-    kl = min(NK, L.it.end - L.it.pos);
-    kr = L.kr;
-    vr = L.vr;
-    L.it.pos += kl;
-    L.kr += NK * kstep;   // a short step ends its run, so this is not used
-    L.vr += NK * vstep;
-    return true;
-  };
-  auto issue_loads = [&](int buf, uint64_t kr, uint64_t vr, int kl) {
+  const uint64_t k1 = kb + (uint64_t)r1s * kstep, v1 = vb + (uint64_t)r1s * vstep;
+  int lj = 0;
+  uint64_t lkr = kb + (uint64_t)r0s * kstep, lvr = vb + (uint64_t)r0s * vstep;
+  // A remainder step (kl < NK keys) reads the NK rows that end at its run's
+  // end when the sequence has that many rows, so its copies take the same
+  // per-lane offsets as a full step's and its live keys are the tile's last
+  // kl rows; otherwise its rows past kl re-read row kl-1 and the live keys
+  // are the first kl rows.
+  const bool shift_short = JINV && p.N >= NK;
+  // first row a remainder step copies, and its live rows' offset in the tile
+  // (a multiple of 16 rows)
+  const int trow0 = shift_short ? max(tend0 - NK, 0) : tpos0, toff0 = tpos0 - trow0;
+  const int trow1 = shift_short ? max(tend1 - NK, 0) : tpos1, toff1 = tpos1 - trow1;
+  auto issue_loads = [&](int buf, uint64_t kr, uint64_t vr, bool fast, int kl) {
     const unsigned kdst = lds_base + 2 * buf * TILEB;
-    const bool fast = JINV && kl == NK;   // wave-uniform
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
       const unsigned row0b = (unsigned)(RPI * (wave + j * W) * ROWB);
@@ -365,12 +346,49 @@ void fwd_bf16_kernel(FwdParams p) {
       }
     }
   };
+  // copies of step lj (< nsteps) into ring buffer buf
+  auto issue_next = [&](int buf) {
+    if (lj < nfull) {
+      if (lj == F0) {
+        lkr = k1;
+        lvr = v1;
+      }
+      issue_loads(buf, lkr, lvr, JINV, NK);
+      lkr += NK * kstep;
+      lvr += NK * vstep;
+    } else {
+      const bool e0 = lj == nfull;
+      const int row = e0 ? trow0 : trow1;
+      issue_loads(buf, kb + (uint64_t)row * kstep, vb + (uint64_t)row * vstep, shift_short, e0 ? tlen0 : tlen1);
+    }
+    ++lj;
+  };
 
-  // One chunk of NS 16-key tiles (NS = 2, or 1 for a 16-key tail) starting
-  // at key row `key0` of the K/V tiles kt/vt.
-  auto chunk = [&](auto fixed_tag, auto ns_tag, const unsigned char *kt, const unsigned char *vt, int key0) {
+  // Per-lane LDS addresses of the MFMA operand reads in a tile at offset 0
+  // of the ring whose first row is a multiple of 16 (both swizzles have
+  // period 16 in the row, so they depend on the lane only); a read adds the
+  // tile's offset, which in the step loop is a constant of the instruction.
+  // K: this lane's 16-byte chunk of row n16 for d slice kd (tile t adds 16
+  // rows). V: the 4 x 16 transposed block of rows 4g + n16/4 (+16 for the
+  // second tile), output tile dt.
+  unsigned kofs[KD], vofs[DT];
+#pragma unroll
+  for (int kd = 0; kd < KD; ++kd) kofs[kd] = lds_base + n16 * ROWB + 16 * ((4 * kd + g) ^ ksw(n16));
+  {
+    const int vr = 4 * g + (n16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vofs[dt] = lds_base + vr * ROWB + 8 * (n16 & 3) + 32 * (dt ^ vsw(vr));
+  }
+  auto kread = [&](unsigned tile, int kd, int t) { return lds_read16(kofs[kd] + tile + 16 * t * ROWB); };
+  auto vread = [&](unsigned tile, int dt, int t) { return lds_read_tr(vofs[dt] + tile + 16 * t * ROWB); };
+
+  // One chunk of NS 16-key tiles (NS = 2, or 1 for a 16-key tail) whose K
+  // rows start at LDS byte offset kt (a multiple of 16 rows into a K tile;
+  // the V rows sit TILEB further).
+  auto chunk = [&](auto fixed_tag, auto ns_tag, unsigned kt) {
     constexpr bool FIXED = decltype(fixed_tag)::value;
     constexpr int NS = decltype(ns_tag)::value;
+    const unsigned vt = kt + TILEB;
     f4 s[M16][NS];
 #pragma unroll
     for (int m = 0; m < M16; ++m)
@@ -384,10 +402,7 @@ void fwd_bf16_kernel(FwdParams p) {
     [[maybe_unused]] bf16x8 ka[KB][NS];
     auto kload = [&](int kd, int slot) {
 #pragma unroll
-      for (int t = 0; t < NS; ++t) {
-        const int r = key0 + 16 * t + n16;
-        ka[slot][t] = *reinterpret_cast<const bf16x8 *>(kt + r * ROWB + 16 * ((4 * kd + g) ^ ksw(r)));
-      }
+      for (int t = 0; t < NS; ++t) ka[slot][t] = kread(kt, kd, t);
     };
     if constexpr (KB == 2) {
       kload(0, 0);
@@ -406,8 +421,7 @@ void fwd_bf16_kernel(FwdParams p) {
       for (int kd = 0; kd < KD; ++kd)
 #pragma unroll
         for (int t = 0; t < NS; ++t) {
-          const int r = key0 + 16 * t + n16;
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kt + r * ROWB + 16 * ((4 * kd + g) ^ ksw(r)));
+          const bf16x8 a = kread(kt, kd, t);
 #pragma unroll
           for (int m = 0; m < M16; ++m) s[m][t] = mfma32(a, qf[m][kd], s[m][t]);
         }
@@ -440,33 +454,17 @@ void fwd_bf16_kernel(FwdParams p) {
         }
       }
     }
-    // V rows of this lane's transposed reads: vr (keys 4g..4g+3 of the first
-    // 16-key tile) and vr + 16; after the swizzle a row's 32-byte segment for
-    // output tile dt sits at byte 32 * (dt ^ vsw(row)). With prefetch the
-    // first VF-1 fragments are requested before the exponentials so that
-    // their latency hides behind them; each PV step then requests fragment
-    // dt+VF-1.
+    // With prefetch the first VF-1 V fragments are requested before the
+    // exponentials so that their latency hides behind them; each PV step
+    // then requests fragment dt+VF-1.
     constexpr int VF = 3;
     constexpr bool VPF = PF && NS == 2;
-    struct VAddr {
-      const unsigned char *v0, *v1;
-      int sw;
-    };
-    auto vaddr = [&]() {
-      const int vr = key0 + 4 * g + (n16 >> 2);
-      const unsigned char *v0 = vt + vr * ROWB + 8 * (n16 & 3);
-      return VAddr{v0, v0 + 16 * ROWB, vsw(vr)};   // vsw(vr + 16) == vsw(vr)
-    };
     bf16x4 va[VF][2];
-    [[maybe_unused]] VAddr pa;
     if constexpr (VPF) {
-      pa = vaddr();
-      const unsigned char *v0 = pa.v0, *v1 = pa.v1;
-      const int sw = pa.sw;
 #pragma unroll
       for (int j = 0; j < VF - 1; ++j) {
-        va[j][0] = lds_read_tr(v0 + 32 * (j ^ sw));
-        va[j][1] = lds_read_tr(v1 + 32 * (j ^ sw));
+        va[j][0] = vread(vt, j, 0);
+        va[j][1] = vread(vt, j, 1);
       }
     }
     bf16x8 pk[M16];
@@ -498,13 +496,11 @@ void fwd_bf16_kernel(FwdParams p) {
       }
     }
     if constexpr (VPF) {
-      const unsigned char *v0 = pa.v0, *v1 = pa.v1;
-      const int sw = pa.sw;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         if (dt + VF - 1 < DT) {
-          va[(dt + VF - 1) % VF][0] = lds_read_tr(v0 + 32 * ((dt + VF - 1) ^ sw));
-          va[(dt + VF - 1) % VF][1] = lds_read_tr(v1 + 32 * ((dt + VF - 1) ^ sw));
+          va[(dt + VF - 1) % VF][0] = vread(vt, dt + VF - 1, 0);
+          va[(dt + VF - 1) % VF][1] = vread(vt, dt + VF - 1, 1);
         }
         __builtin_amdgcn_sched_barrier(0);
         const bf16x8 a = __builtin_shufflevector(va[dt % VF][0], va[dt % VF][1], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -513,19 +509,14 @@ void fwd_bf16_kernel(FwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
-      const VAddr a0 = vaddr();
-      const unsigned char *v0 = a0.v0, *v1 = a0.v1;
-      const int sw = a0.sw;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         if constexpr (NS == 2) {
-          const bf16x4 lo = lds_read_tr(v0 + 32 * (dt ^ sw));
-          const bf16x4 hi = lds_read_tr(v1 + 32 * (dt ^ sw));
-          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          const bf16x8 a = __builtin_shufflevector(vread(vt, dt, 0), vread(vt, dt, 1), 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
           for (int m = 0; m < M16; ++m) oacc[m][dt] = mfma32(a, pk[m], oacc[m][dt]);
         } else {
-          const bf16x4 a = lds_read_tr(v0 + 32 * (dt ^ sw));
+          const bf16x4 a = vread(vt, dt, 0);
 #pragma unroll
           for (int m = 0; m < M16; ++m) oacc[m][dt] = mfma16(a, pt[m], oacc[m][dt]);
         }
@@ -533,56 +524,64 @@ void fwd_bf16_kernel(FwdParams p) {
     }
   };
   // The step loop, instantiated once per softmax path so that the two
-  // paths never merge inside it.
-  auto main_loop = [&](auto fixed_tag) {
-    LIter li;
-    Iter ci;
-    liter_init(li);
-    iter_init(ci);
-    int issued = 0;
+  // paths never merge inside it (idle waves run it with copies only). It is
+  // unrolled by the ring depth, so each step's buffer offset is a constant
+  // that folds into the LDS instructions.
+  auto main_loop = [&](auto fixed_tag, auto compute_tag) {
+    constexpr bool COMPUTE = decltype(compute_tag)::value;
 #pragma unroll
-    for (int j = 0; j < NBUF - 1; ++j) {
-      int kl = 0;
-      uint64_t kr = 0, vr = 0;
-      if (lnext(li, kl, kr, vr)) {
-        issue_loads(j, kr, vr, kl);
-        ++issued;
-      }
-    }
-    int step = 0, ckl = 0;
-    while (next_step(ci, ckl)) {
-      // my copies of this step are done once at most (issued - step - 1)
-      // later steps' copies are outstanding
-      const int later = issued - step - 1;
-      if (later >= NBUF - 1) wait_vmcnt<(NBUF - 1) * LPW>();
-      else if (NBUF > 3 && later == 2) wait_vmcnt<(NBUF > 3 ? 2 * LPW : 0)>();
-      else if (NBUF > 2 && later == 1) wait_vmcnt<(NBUF > 2 ? LPW : 0)>();
+    for (int j = 0; j < NBUF - 1; ++j)
+      if (lj < nsteps) issue_next(j);
+    // step i's copies in: wait, publish, refill the buffer step i-1 used
+    auto step_in = [&](int i, int buf) {
+      // my copies of step i are done once at most NBUF-2 later steps'
+      // copies are outstanding
+      if (i + NBUF - 2 < nsteps) wait_vmcnt<(NBUF - 2) * LPW>();
       else wait_vmem();
-      __syncthreads();   // every wave's copies of this step landed; step-1 is free
-      {
-        int kl = 0;
-        uint64_t kr = 0, vr = 0;
-        if (lnext(li, kl, kr, vr)) {
-          issue_loads((step + NBUF - 1) % NBUF, kr, vr, kl);
-          ++issued;
-        }
+      __syncthreads();   // every wave's copies of step i landed; step i-1's buffer is free
+      if (lj < nsteps) issue_next((buf + NBUF - 1) % NBUF);
+    };
+    auto full_step = [&](int i, int buf) {
+      step_in(i, buf);
+      if constexpr (COMPUTE) {
+#pragma unroll
+        for (int c = 0; c < NK / 32; ++c)
+          chunk(fixed_tag, std::integral_constant<int, 2>{}, 2 * buf * TILEB + 32 * c * ROWB);
       }
-      const unsigned char *kt = smem + 2 * (step % NBUF) * TILEB;
-      const unsigned char *vt = kt + TILEB;
-      if (active) {
-        const int full = ckl >> 5;
-        for (int c = 0; c < full; ++c) chunk(fixed_tag, std::integral_constant<int, 2>{}, kt, vt, 32 * c);
-        if (ckl & 16) chunk(fixed_tag, std::integral_constant<int, 1>{}, kt, vt, ckl - 16);
+    };
+    int i = 0;
+    // full steps, unrolled by the ring depth: each buffer offset is a
+    // constant of the LDS instructions
+    for (; i + NBUF <= nfull; i += NBUF) {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) full_step(i + u, u);
+    }
+    for (; i < nfull; ++i) full_step(i, i % NBUF);
+    // remainder steps
+    for (; i < nsteps; ++i) {
+      const int buf = i % NBUF;
+      step_in(i, buf);
+      if constexpr (COMPUTE) {
+        const bool e0 = i == nfull;
+        const int kl = e0 ? tlen0 : tlen1;
+        // the step's first live row in the tile
+        const unsigned k0 = 2 * buf * TILEB + (unsigned)(e0 ? toff0 : toff1) * ROWB;
+#pragma unroll
+        for (int c = 0; c < NK / 32 - 1; ++c)
+          if (c < (kl >> 5)) chunk(fixed_tag, std::integral_constant<int, 2>{}, k0 + 32 * c * ROWB);
+        if (kl & 16) chunk(fixed_tag, std::integral_constant<int, 1>{}, k0 + (kl & ~31) * ROWB);
       }
-      ++step;
     }
   };
+  if (!active) {
+    main_loop(std::true_type{}, std::false_type{});
+    return;
+  }
   if (fixed)
-    main_loop(std::true_type{});
+    main_loop(std::true_type{}, std::true_type{});
   else
-    main_loop(std::false_type{});
+    main_loop(std::false_type{}, std::true_type{});
 
-  if (!active) return;
   // Epilogue: one cross-lane reduction of the row sums, normalise, store.
 #pragma unroll
   for (int m = 0; m < M16; ++m) {
