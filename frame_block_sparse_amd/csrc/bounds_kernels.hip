@@ -6,11 +6,10 @@
 // Four launches; the two passes stream Q and K (HBM-bound), the other two
 // are small:
 //   pass1   per (token chunk, head): partial key sums, partial max |q|^2
-//   frames  per (frame, head): the frame's key sum from its chunks
-//   pass2   per (token chunk, head): key mean from the frame sums, partial
-//           max |k - mu|^2
-//   final   per head: max |q|, max |k - mu|, c_max from the frame sums,
-//           bound, gap estimate, eligibility
+//   head    per head: the frame key sums from their chunks, the key mean,
+//           c_max from the frame sums, max |q|
+//   pass2   per (token chunk, head): partial max |k - mu|^2
+//   final   per head: max |k - mu|, bound, gap estimate, eligibility
 // Chunks never cross a frame, so the per-frame sums are sums of whole
 // chunks. Every reduction has a fixed order and no atomics are used, so the
 // results are bitwise reproducible run to run.
@@ -52,16 +51,18 @@ __device__ inline float row_sum(float v, int width) {
   return v;
 }
 
+// Maximum over the workgroup (NT threads): within each wave by lane
+// exchange, then over the waves' results in LDS (sh holds NT/64 floats).
+// Every thread returns the maximum.
+template <int NT>
 __device__ inline float block_max(float v, float *sh) {
-  const int t = threadIdx.x;
-  sh[t] = v;
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();   // sh may still be read by a previous call
+  if ((threadIdx.x & 63) == 0) sh[wave] = v;
   __syncthreads();
-  for (int o = kThreads / 2; o > 0; o >>= 1) {
-    if (t < o) sh[t] = fmaxf(sh[t], sh[t + o]);
-    __syncthreads();
-  }
-  const float r = sh[0];
-  __syncthreads();
+  float r = sh[0];
+  for (int w = 1; w < NT / 64; ++w) r = fmaxf(r, sh[w]);
   return r;
 }
 
@@ -92,8 +93,9 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void bounds_pass1(BoundsParams p) {
   constexpr int TPR = D / 8;            // threads per token row (8 elements each)
   constexpr int RPP = kThreads / TPR;   // rows per pass
+  constexpr int U = 4;                  // passes whose loads are issued together
   __shared__ float sh[RPP][D + 1];
-  __shared__ float red[kThreads];
+  __shared__ float red[kThreads / 64];
   const int c = blockIdx.x, bh = blockIdx.y;
   const int b = bh / p.H, h = bh % p.H;
   const int NC = p.F * p.chunks_per_frame;
@@ -104,17 +106,28 @@ __global__ __launch_bounds__(kThreads) void bounds_pass1(BoundsParams p) {
   chunk_range(p, c, &t0, &t1);
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float qm = 0.f;
-  for (int t = t0 + r; t < t1; t += RPP) {
-    float x[8], y[8];
-    load8<T>(k + (int64_t)t * p.ksn, x);
-    load8<T>(q + (int64_t)t * p.qsn, y);
-    float s = 0.f;
+  for (int t = t0 + r; t < t1; t += U * RPP) {
+    float x[U][8], y[U][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      acc[e] += x[e];
-      s = fmaf(y[e], y[e], s);
+    for (int u = 0; u < U; ++u) {
+      if (t + u * RPP < t1) {
+        load8<T>(k + (int64_t)(t + u * RPP) * p.ksn, x[u]);
+        load8<T>(q + (int64_t)(t + u * RPP) * p.qsn, y[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[u][e] = y[u][e] = 0.f;
+      }
     }
-    qm = fmaxf(qm, row_sum(s, TPR));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        acc[e] += x[u][e];
+        s = fmaf(y[u][e], y[u][e], s);
+      }
+      qm = fmaxf(qm, row_sum(s, TPR));
+    }
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) sh[r][col * 8 + e] = acc[e];
@@ -124,92 +137,55 @@ __global__ __launch_bounds__(kThreads) void bounds_pass1(BoundsParams p) {
     for (int i = 0; i < RPP; ++i) s += sh[i][threadIdx.x];
     p.ws_part[((int64_t)bh * NC + c) * D + threadIdx.x] = s;
   }
-  const float m = block_max(qm, red);
+  const float m = block_max<kThreads>(qm, red);
   if (threadIdx.x == 0) p.ws_qmax[(int64_t)bh * NC + c] = m;
 }
 
-// Per (frame, head): the frame's key sum from its chunks' partial sums, in
-// chunk order.
+constexpr int kHeadThreads = 512;
+constexpr int kHeadLdsFloats = 12288;   // frame sums staged in LDS up to this size (48 KB)
+
+// Per head: the frame key sums (each the sum of its chunks' partial sums in
+// chunk order), the key mean (frame sums added in frame order, divided by
+// N), c_max from the frame sums, and max |q| from the chunk maxima.
 template <int D>
-__global__ __launch_bounds__(D) void bounds_frames(BoundsParams p) {
-  const int f = blockIdx.x, bh = blockIdx.y;
-  const int NC = p.F * p.chunks_per_frame;
-  const int j = threadIdx.x;
-  const float *part = p.ws_part + ((int64_t)bh * NC + (int64_t)f * p.chunks_per_frame) * D + j;
-  p.ws_frame[((int64_t)bh * p.F + f) * D + j] = ordered_sum(part, p.chunks_per_frame, D);
-}
-
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void bounds_pass2(BoundsParams p) {
-  constexpr int TPR = D / 8;
-  constexpr int RPP = kThreads / TPR;
-  __shared__ float red[kThreads];
-  __shared__ float mu_sh[D];
-  const int c = blockIdx.x, bh = blockIdx.y;
-  const int b = bh / p.H, h = bh % p.H;
-  const int NC = p.F * p.chunks_per_frame;
-  // key mean of the head: frame sums added in frame order, divided by N
-  // (every workgroup of the head computes the same bits; chunk 0 stores it)
-  if (threadIdx.x < D) {
-    const float *S = p.ws_frame + (int64_t)bh * p.F * D + threadIdx.x;
-    const float mu = ordered_sum(S, p.F, D) / (float)p.N;
-    mu_sh[threadIdx.x] = mu;
-    if (c == 0) p.key_mean[(int64_t)bh * D + threadIdx.x] = mu;
-  }
-  __syncthreads();
-  const int col = threadIdx.x % TPR, r = threadIdx.x / TPR;
-  const T *k = static_cast<const T *>(p.k) + b * p.ksb + h * p.ksh + col * 8;
-  float mu[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) mu[e] = mu_sh[col * 8 + e];
-  int t0, t1;
-  chunk_range(p, c, &t0, &t1);
-  float km = 0.f;
-  for (int t = t0 + r; t < t1; t += RPP) {
-    float x[8];
-    load8<T>(k + (int64_t)t * p.ksn, x);
-    float s = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float dlt = x[e] - mu[e];
-      s = fmaf(dlt, dlt, s);
-    }
-    km = fmaxf(km, row_sum(s, TPR));
-  }
-  const float m = block_max(km, red);
-  if (threadIdx.x == 0) p.ws_kmax[(int64_t)bh * NC + c] = m;
-}
-
-constexpr int kFinalLdsFloats = 12288;   // frame sums staged in LDS up to this size (48 KB)
-
-template <int D>
-__global__ __launch_bounds__(kThreads) void bounds_final(BoundsParams p) {
+__global__ __launch_bounds__(kHeadThreads) void bounds_head(BoundsParams p) {
   constexpr int PER_LANE = D / 64;
-  __shared__ float red[kThreads];
-  __shared__ float S_sh[kFinalLdsFloats];
+  constexpr int NW = kHeadThreads / 64;
+  __shared__ float red[NW];
+  __shared__ float S_sh[kHeadLdsFloats];
+  __shared__ float mu_sh[D];
   const int bh = blockIdx.x;
   const int NC = p.F * p.chunks_per_frame;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const float *Sg = p.ws_frame + (int64_t)bh * p.F * D;
-  const bool staged = p.F * D <= kFinalLdsFloats;
-  if (staged)
-    for (int i = threadIdx.x; i < p.F * D; i += kThreads) S_sh[i] = Sg[i];
-  float km = 0.f, qm = 0.f;
-  for (int c = threadIdx.x; c < NC; c += kThreads) {
-    km = fmaxf(km, p.ws_kmax[(int64_t)bh * NC + c]);
-    qm = fmaxf(qm, p.ws_qmax[(int64_t)bh * NC + c]);
+  // frame sums, wave w taking frames w, w + NW, ...; kept in LDS when they
+  // fit, else in the workspace
+  const bool staged = p.F * D <= kHeadLdsFloats;
+  float *S = staged ? S_sh : p.ws_frame + (int64_t)bh * p.F * D;
+  for (int f = wave; f < p.F; f += NW) {
+    const float *part = p.ws_part + ((int64_t)bh * NC + (int64_t)f * p.chunks_per_frame) * D;
+#pragma unroll
+    for (int e = 0; e < PER_LANE; ++e)
+      S[(int64_t)f * D + lane + 64 * e] = ordered_sum(part + lane + 64 * e, p.chunks_per_frame, D);
   }
-  km = block_max(km, red);   // (its barriers also publish S_sh)
-  qm = block_max(qm, red);
+  if (!staged) __threadfence();
+  __syncthreads();
+  if (!staged) __threadfence();
+  if (threadIdx.x < D) {
+    const float mu = ordered_sum(S + threadIdx.x, p.F, D) / (float)p.N;
+    mu_sh[threadIdx.x] = mu;
+    p.key_mean[(int64_t)bh * D + threadIdx.x] = mu;
+  }
+  float qm = 0.f;
+  for (int c = threadIdx.x; c < NC; c += kHeadThreads) qm = fmaxf(qm, p.ws_qmax[(int64_t)bh * NC + c]);
+  qm = block_max<kHeadThreads>(qm, red);   // (its barriers also publish mu_sh)
   float mu[PER_LANE];
 #pragma unroll
-  for (int e = 0; e < PER_LANE; ++e) mu[e] = p.key_mean[(int64_t)bh * D + lane + 64 * e];
-  const float *S = staged ? S_sh : Sg;
+  for (int e = 0; e < PER_LANE; ++e) mu[e] = mu_sh[lane + 64 * e];
   // c_max: the largest distance between the mean of the keys a query frame
   // sees (its window plus the reference frame) and the head's key mean.
   // One wave per frame; the squared distance is summed over the wave.
   float cm = 0.f;
-  for (int f = wave; f < p.F; f += kThreads / 64) {
+  for (int f = wave; f < p.F; f += NW) {
     const int lo = max(0, f - p.wr), hi = min(p.F - 1, f + p.wa);
     const bool extra = p.ref >= 0 && (p.ref < lo || p.ref > hi);
     const float cnt = (float)(hi - lo + 1 + (extra ? 1 : 0)) * (float)p.T;
@@ -227,15 +203,70 @@ __global__ __launch_bounds__(kThreads) void bounds_final(BoundsParams p) {
     for (int o = 32; o > 0; o >>= 1) dd += __shfl_xor(dd, o, 64);
     cm = fmaxf(cm, dd);
   }
-  cm = block_max(cm, red);
+  cm = block_max<kHeadThreads>(cm, red);
   if (threadIdx.x == 0) {
-    const float qn = sqrtf(qm);
+    p.rec[bh].q_norm_max = sqrtf(qm);
+    p.rec[bh].c_max = sqrtf(cm);
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void bounds_pass2(BoundsParams p) {
+  constexpr int TPR = D / 8;
+  constexpr int RPP = kThreads / TPR;
+  constexpr int U = 4;
+  __shared__ float red[kThreads / 64];
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / p.H, h = bh % p.H;
+  const int NC = p.F * p.chunks_per_frame;
+  const int col = threadIdx.x % TPR, r = threadIdx.x / TPR;
+  const T *k = static_cast<const T *>(p.k) + b * p.ksb + h * p.ksh + col * 8;
+  float mu[8];   // the key mean from the head pass
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mu[e] = p.key_mean[(int64_t)bh * D + col * 8 + e];
+  int t0, t1;
+  chunk_range(p, c, &t0, &t1);
+  float km = 0.f;
+  for (int t = t0 + r; t < t1; t += U * RPP) {
+    float x[U][8];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      ok[u] = t + u * RPP < t1;
+      if (ok[u]) load8<T>(k + (int64_t)(t + u * RPP) * p.ksn, x[u]);
+      else
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[u][e] = mu[e];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float dlt = x[u][e] - mu[e];
+        s = fmaf(dlt, dlt, s);
+      }
+      km = fmaxf(km, row_sum(s, TPR));
+    }
+  }
+  const float m = block_max<kThreads>(km, red);
+  if (threadIdx.x == 0) p.ws_kmax[(int64_t)bh * NC + c] = m;
+}
+
+// Per head: max |k - mu| from the chunk maxima, then the bound, the gap
+// estimate and eligibility.
+__global__ __launch_bounds__(kThreads) void bounds_final(BoundsParams p) {
+  __shared__ float red[kThreads / 64];
+  const int bh = blockIdx.x;
+  const int NC = p.F * p.chunks_per_frame;
+  float km = 0.f;
+  for (int c = threadIdx.x; c < NC; c += kThreads) km = fmaxf(km, p.ws_kmax[(int64_t)bh * NC + c]);
+  km = block_max<kThreads>(km, red);
+  if (threadIdx.x == 0) {
+    fsattn_head_bound r = p.rec[bh];   // q_norm_max and c_max from the head pass
+    const float qn = r.q_norm_max, cn = r.c_max;
     const float kn = sqrtf(km);
-    const float cn = sqrtf(cm);
-    fsattn_head_bound r;
-    r.q_norm_max = qn;
     r.k_norm_max = kn;
-    r.c_max = cn;
     r.bound = p.scale * qn * kn;
     r.gap_est = p.scale * qn * (kn + cn);
     r.eligible = r.gap_est <= p.threshold ? 1 : 0;
@@ -249,9 +280,9 @@ hipError_t launch_all(const BoundsParams &p, hipStream_t st) {
   const int BH = p.B * p.H;
   const int NC = p.F * p.chunks_per_frame;
   hipLaunchKernelGGL((bounds_pass1<T, D>), dim3(NC, BH), dim3(kThreads), 0, st, p);
-  hipLaunchKernelGGL((bounds_frames<D>), dim3(p.F, BH), dim3(D), 0, st, p);
+  hipLaunchKernelGGL((bounds_head<D>), dim3(BH), dim3(kHeadThreads), 0, st, p);
   hipLaunchKernelGGL((bounds_pass2<T, D>), dim3(NC, BH), dim3(kThreads), 0, st, p);
-  hipLaunchKernelGGL((bounds_final<D>), dim3(BH), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL(bounds_final, dim3(BH), dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 

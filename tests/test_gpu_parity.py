@@ -115,6 +115,12 @@ SMALL = [
     ("dense", 1, 2, 3, 256, 128, "bf16", 3, 3, 0, 64, 64),
     ("d64", 2, 2, 5, 96, 64, "bf16", 1, 1, 0, 48, 16),
     ("single_frame", 1, 1, 1, 64, 128, "bf16", 0, 0, -1, 16, 64),
+    # 16-token frames: the reference frame is a 16-key run ending before
+    # key 32, so its copy cannot start 32 rows before its end
+    ("ref16_clamp", 1, 2, 6, 16, 128, "bf16", 1, 1, 0, 16, 16),
+    ("ref16_clamp_d64", 2, 1, 3, 16, 64, "bf16", 1, 0, -1, 16, 16),
+    # a sequence shorter than one 32-key step
+    ("tiny16", 1, 1, 1, 16, 128, "bf16", 0, 0, -1, 16, 16),
     ("f32_d128", 1, 2, 4, 80, 128, "f32", 1, 1, 0, 16, 80),
     ("f32_d64", 2, 1, 6, 48, 64, "f32", 0, 2, 5, 48, 16),
 ]
