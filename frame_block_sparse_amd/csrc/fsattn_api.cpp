@@ -77,6 +77,18 @@ extern "C" const char *fsattn_status_string(fsattn_status st) {
   return "unknown status";
 }
 
+extern "C" fsattn_status fsattn_plan_device(void *hip_stream, const fsattn_mask *m, int32_t *row_ptr,
+                                            int64_t row_ptr_len, int32_t *col_idx, int64_t col_idx_len) {
+  if (!m || !row_ptr || (!col_idx && col_idx_len > 0)) return FSATTN_ERR_INVALID_ARGUMENT;
+  int64_t nqb = 0, nnz = 0;
+  fsattn_status st = fsattn_plan_size(m, &nqb, &nnz);
+  if (st != FSATTN_OK) return st;
+  if (nnz > INT32_MAX) return FSATTN_ERR_UNSUPPORTED;
+  if (row_ptr_len < nqb + 1 || col_idx_len < nnz) return FSATTN_ERR_BUFFER_TOO_SMALL;
+  const hipError_t e = launch_plan_device(*m, row_ptr, col_idx, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? FSATTN_OK : FSATTN_ERR_HIP;
+}
+
 extern "C" size_t fsattn_head_bounds_workspace_bytes(const fsattn_shape *s, const fsattn_mask *m) {
   if (check_shape(s, m) != FSATTN_OK) return 0;
   return ws_layout(s, m).total;

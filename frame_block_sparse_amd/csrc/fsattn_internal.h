@@ -35,6 +35,9 @@ struct BoundsParams {
 
 hipError_t launch_head_bounds(const BoundsParams &p, int dtype, hipStream_t st);
 
+// Device plan (same arrays as fsattn_plan); the mask is already validated.
+hipError_t launch_plan_device(const fsattn_mask &m, int32_t *row_ptr, int32_t *col_idx, hipStream_t st);
+
 struct FwdParams {
   const void *q, *k, *v;
   void *o;

@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
     c_i64p = ctypes.POINTER(ctypes.c_int64)
     L.fsattn_plan_size.argtypes = [ctypes.POINTER(Mask), c_i64p, c_i64p]
     L.fsattn_plan.argtypes = [ctypes.POINTER(Mask), c_i32p, ctypes.c_int64, c_i32p, ctypes.c_int64]
+    L.fsattn_plan_device.argtypes = [ctypes.c_void_p, ctypes.POINTER(Mask), ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.c_void_p, ctypes.c_int64]
     L.fsattn_head_bounds_workspace_bytes.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Mask)]
     L.fsattn_head_bounds_workspace_bytes.restype = ctypes.c_size_t
     L.fsattn_head_bounds.argtypes = [ctypes.c_void_p, ctypes.POINTER(Shape), ctypes.POINTER(Mask), Tensor, Tensor,
@@ -85,7 +87,7 @@ def lib() -> ctypes.CDLL:
     L.fsattn_status_string.argtypes = [ctypes.c_int]
     L.fsattn_status_string.restype = ctypes.c_char_p
     L.fsattn_abi_version.argtypes = []
-    for name in ("fsattn_plan_size", "fsattn_plan", "fsattn_head_bounds", "fsattn_forward",
+    for name in ("fsattn_plan_size", "fsattn_plan", "fsattn_plan_device", "fsattn_head_bounds", "fsattn_forward",
                  "fsattn_forward_launch_info"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -181,11 +183,29 @@ class DevicePlan:
 
 
 def device_plan(mask, device) -> DevicePlan:
+    """The host plan (fsattn_plan) copied to the device."""
     m = to_mask(mask)
     rp, ci = plan(m)
     if ci.numel() == 0:
         ci = torch.zeros(1, dtype=torch.int32)[:0]
     return DevicePlan(m, rp.to(device), ci.to(device))
+
+
+def plan_on_device(mask, device=None, out: Optional[DevicePlan] = None) -> DevicePlan:
+    """The plan written on the GPU by fsattn_plan_device, on the current
+    stream; `out` reuses the device arrays of an earlier plan of the same
+    mask. Both arrays live in one buffer (row_ptr, then col_idx)."""
+    m = to_mask(mask)
+    nqb, nnz = plan_size(m)
+    if out is None:
+        buf = torch.empty(nqb + 1 + nnz, dtype=torch.int32, device=device)
+        out = DevicePlan(m, buf[:nqb + 1], buf[nqb + 1:])
+    elif out.row_ptr.numel() != nqb + 1 or out.col_idx.numel() != nnz:
+        raise ValueError("out holds a plan of another size")
+    stream = torch.cuda.current_stream(out.row_ptr.device).cuda_stream
+    _check(lib().fsattn_plan_device(stream, ctypes.byref(m), out.row_ptr.data_ptr(), out.row_ptr.numel(),
+                                    out.col_idx.data_ptr(), out.col_idx.numel()), "fsattn_plan_device")
+    return out
 
 
 # ----------------------------------------------------------------- bounds

@@ -3,6 +3,7 @@
  *
  * C ABI of the library libfsattn.so. Three calls make the hot path:
  *   fsattn_plan         live key blocks per query block (host, bit-exact)
+ *                       (fsattn_plan_device: the same arrays written on the GPU)
  *   fsattn_head_bounds  key mean, norm maxima, logit bound, eligibility (GPU)
  *   fsattn_forward      attention over the live blocks, fixed-shift or
  *                       online softmax chosen per head (GPU)
@@ -155,6 +156,18 @@ fsattn_status fsattn_plan_size(const fsattn_mask *m, int64_t *num_q_blocks, int6
  */
 fsattn_status fsattn_plan(const fsattn_mask *m, int32_t *row_ptr, int64_t row_ptr_len,
                           int32_t *col_idx, int64_t col_idx_len);
+
+/*
+ * The same plan as fsattn_plan, element for element, written by a GPU
+ * kernel into caller-owned DEVICE memory (row_ptr[num_q_blocks + 1],
+ * col_idx[nnz]), so that a pipeline needs no host-to-device copy of it.
+ * The lengths are those of the device buffers. Validation is on the host
+ * and identical to fsattn_plan's; asynchronous on hip_stream.
+ * Errors: INVALID_ARGUMENT, BLOCK_GEOMETRY, UNSUPPORTED (nnz > INT32_MAX),
+ * BUFFER_TOO_SMALL, HIP.
+ */
+fsattn_status fsattn_plan_device(void *hip_stream, const fsattn_mask *m, int32_t *row_ptr,
+                                 int64_t row_ptr_len, int32_t *col_idx, int64_t col_idx_len);
 
 /* Bytes of device workspace fsattn_head_bounds needs for this shape and
  * mask; 0 if the arguments are invalid. */

@@ -86,6 +86,19 @@ def test_plan_buffer_too_small_leaves_output_untouched():
     assert st == 4
 
 
+def test_plan_device_validates_on_host():
+    """fsattn_plan_device rejects what fsattn_plan rejects, before any
+    launch (the device pointers here are never dereferenced)."""
+    L = fs.lib()
+    good = F.to_mask((5, 48, 1, 1, 0, 16, 16))        # 16 query blocks, 143 entries
+    bad = F.to_mask((5, 48, 1, 1, 0, 24, 16))
+    assert L.fsattn_plan_device(None, ctypes.byref(bad), FAKE, 16, FAKE, 143) == 2
+    assert L.fsattn_plan_device(None, ctypes.byref(good), FAKE, 15, FAKE, 143) == 4
+    assert L.fsattn_plan_device(None, ctypes.byref(good), FAKE, 16, FAKE, 142) == 4
+    assert L.fsattn_plan_device(None, ctypes.byref(good), None, 16, FAKE, 143) == 1
+    assert L.fsattn_plan_device(None, None, FAKE, 16, FAKE, 143) == 1
+
+
 # ---- argument validation of the GPU entry points (host-side, nothing launched)
 
 FAKE = 0x7f0000000000          # 16-byte aligned, never dereferenced: every call below fails validation

@@ -76,6 +76,37 @@ def _sample_rows(w, per_frame, seed):
 # ------------------------------------------------------------------ bounds
 
 @pytest.mark.parametrize("i", [1, 2, 3, 4, 5])
+def test_plan_device_bit_exact_on_workloads(dev, i):
+    """fsattn_plan_device writes the host plan's arrays element for element."""
+    w = workloads.config(i)
+    _say(f"[plan-device] {w.name}")
+    rp, ci = fs.plan(w)
+    dp = fs.plan_on_device(w, dev)
+    torch.cuda.synchronize()
+    assert torch.equal(dp.row_ptr.cpu(), rp) and torch.equal(dp.col_idx.cpu(), ci)
+
+
+def test_plan_device_bit_exact_on_random_geometries(dev):
+    rng = np.random.default_rng(11)
+    cases = [(3, 32, 10 ** 6, 10 ** 6, 1, 16, 32), (1, 16, 0, 0, -1, 16, 16), (7, 48, 0, 2, 6, 48, 16)]
+    for _ in range(40):
+        T = 16 * int(rng.integers(1, 7))
+        divs = [b for b in range(16, T + 1, 16) if T % b == 0]
+        F_ = int(rng.integers(1, 12))
+        cases.append((F_, T, int(rng.integers(0, 4)), int(rng.integers(0, 4)), int(rng.integers(-1, F_)),
+                      int(rng.choice(divs)), int(rng.choice(divs))))
+    for g in cases:
+        rp, ci = fs.plan(g)
+        dp = fs.plan_on_device(g, dev)
+        torch.cuda.synchronize()
+        assert torch.equal(dp.row_ptr.cpu(), rp), g
+        assert torch.equal(dp.col_idx.cpu(), ci), g
+        if g[0] * g[1] <= 400:
+            orp, oci = oracle.plan_bruteforce(oracle.MaskGeometry(*g))
+            assert np.array_equal(rp.numpy(), orp) and np.array_equal(ci.numpy(), oci), g
+
+
+@pytest.mark.parametrize("i", [1, 2, 3, 4, 5])
 def test_head_bounds_parity(dev, config_inputs, i):
     w = workloads.config(i)
     _say(f"[bounds] workload {i} {w.name}")
