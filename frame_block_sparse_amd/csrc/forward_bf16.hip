@@ -182,8 +182,6 @@ void fwd_bf16_kernel(FwdParams p) {
   // d = 128 (one full bank row), 128 bytes for d = 64 (two rows per bank row).
   auto ksw = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
   auto vsw = [](int r) { return D == 128 ? (r & 7) : ((r >> 1) & 3); };
-  constexpr int LPW = 2 * NI / W;     // copies per wave per step
-  static_assert(NI % W == 0, "copies must split evenly over the waves");
   static_assert(NBUF >= 2, "ring of at least two buffers");
 
   extern __shared__ __align__(16) unsigned char smem[];
@@ -193,6 +191,7 @@ void fwd_bf16_kernel(FwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(wave >= 0 && wave < W);
   const int g = lane >> 4, n16 = lane & 15;
   int f, bh, ti;
   map_block(p, blockIdx.x, f, bh, ti);
@@ -286,33 +285,42 @@ void fwd_bf16_kernel(FwdParams p) {
   const int tpos1 = r1s + NK * F1, tend1 = r1e, tlen1 = t1;
 
   // Global -> LDS copies. A tile of NK rows is NI wave-wide copies of RPI
-  // rows; wave w issues copies w, w + W, ... of K, then the same of V
-  // (NI is a multiple of W). Lane l writes physical chunk l % CPR of row
-  // RPI*copy + l / CPR, which holds the logical chunk given by the tile's
-  // swizzle; its source offset within the step is fixed, so it is computed
-  // once (rows past a short step re-read the step's last row).
-  constexpr int CPT = NI / W;         // copies per wave per tile
+  // rows (copy c holds rows RPI*c ..). Lane l writes physical chunk l % CPR
+  // of row RPI*c + l / CPR, which holds the logical chunk given by the
+  // tile's swizzle. Both swizzles have period 16 rows, so copies whose rows
+  // differ by a multiple of 16 read the same chunk of their rows: they form
+  // one of G = 16 / RPI groups per tensor (copies p, p + G, ...), and a
+  // lane's source offset within a full step is one value per group. The 2G
+  // groups (K, then V) are dealt to the waves round-robin: wave w owns groups
+  // w, w + W, ... (with more waves than groups some waves copy nothing).
+  constexpr int G = 16 / RPI;             // groups per tensor
+  constexpr int CPG = NI / G;             // copies per group per tile
+  constexpr int GPW = (2 * G + W - 1) / W;   // group slots per wave
+  static_assert(NI % G == 0, "a tile holds whole groups");
+  // every wave owns the same number of groups (then a wave knows how many
+  // of its copies are in flight per step)
+  constexpr bool EVEN = (2 * G) % W == 0;
+  constexpr int LPW = EVEN ? 2 * G / W * CPG : 0;   // copies per wave per step
   const int lrow = lane / CPR, lchunk = lane % CPR;
   // Byte offsets within a step are 32-bit (the host guarantees that 64 rows
   // of either tensor span less than 2^31 bytes).
   const unsigned kstride2 = (unsigned)(2 * p.ksn), vstride2 = (unsigned)(2 * p.vsn);
   const unsigned lds_base = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_uchar *)smem);
-  auto src_off = [&](int j, int kl, unsigned &ko, unsigned &vo) {
-    const int r = RPI * (wave + j * W) + lrow;
+  // this lane's source offset for copy c of K (or V) when the step has kl
+  // rows (rows past kl re-read row kl - 1)
+  auto src_off = [&](bool isv, int c, int kl) -> unsigned {
+    const int r = RPI * c + lrow;
     const unsigned rs = (unsigned)min(r, kl - 1);
-    const unsigned ck = lchunk ^ ksw(r);
-    const unsigned cv = (((lchunk >> 1) ^ vsw(r)) << 1) | (lchunk & 1);
-    ko = rs * kstride2 + 16u * ck;
-    vo = rs * vstride2 + 16u * cv;
+    if (!isv) return rs * kstride2 + 16u * (lchunk ^ ksw(r));
+    return rs * vstride2 + 16u * ((((lchunk >> 1) ^ vsw(r)) << 1) | (lchunk & 1));
   };
-  // A wave's successive copies are RPI * W rows apart. When that is a
-  // multiple of 16 (the period of both swizzles), every copy of a full step
-  // reads the same chunk of its row, so a lane's offset is one fixed value
-  // per tensor and the copy's row distance goes into the wave-uniform base.
-  constexpr int JROWS = RPI * W;
-  constexpr bool JINV = JROWS % 16 == 0;
-  unsigned koff0 = 0, voff0 = 0;
-  if constexpr (JINV) src_off(0, NK, koff0, voff0);
+  // the wave's groups and each one's lane offset in a full step
+  unsigned goff[GPW];
+#pragma unroll
+  for (int sl = 0; sl < GPW; ++sl) {
+    const int gi = wave + sl * W;
+    goff[sl] = gi < 2 * G ? src_off(gi >= G, gi % G, NK) : 0u;
+  }
   // The copy side walks the steps in order with the byte addresses of its
   // next step's first K and V rows, advanced by one step's stride and set
   // to run 1's first row when it gets there.
@@ -325,24 +333,27 @@ void fwd_bf16_kernel(FwdParams p) {
   // per-lane offsets as a full step's and its live keys are the tile's last
   // kl rows; otherwise its rows past kl re-read row kl-1 and the live keys
   // are the first kl rows.
-  const bool shift_short = JINV && p.N >= NK;
+  const bool shift_short = p.N >= NK;
   // first row a remainder step copies, and its live rows' offset in the tile
   // (a multiple of 16 rows)
   const int trow0 = shift_short ? max(tend0 - NK, 0) : tpos0, toff0 = tpos0 - trow0;
   const int trow1 = shift_short ? max(tend1 - NK, 0) : tpos1, toff1 = tpos1 - trow1;
   auto issue_loads = [&](int buf, uint64_t kr, uint64_t vr, bool fast, int kl) {
-    const unsigned kdst = lds_base + 2 * buf * TILEB;
+    const unsigned tile = lds_base + 2 * buf * TILEB;
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      const unsigned row0b = (unsigned)(RPI * (wave + j * W) * ROWB);
-      if (fast) {
-        dma16(kr + (uint64_t)(j * JROWS) * kstep, koff0, kdst + row0b);
-        dma16(vr + (uint64_t)(j * JROWS) * vstep, voff0, kdst + TILEB + row0b);
-      } else {
-        unsigned ko, vo;
-        src_off(j, kl, ko, vo);
-        dma16(kr, ko, kdst + row0b);
-        dma16(vr, vo, kdst + TILEB + row0b);
+    for (int sl = 0; sl < GPW; ++sl) {
+      const int gi = wave + sl * W;   // wave-uniform
+      if (gi < 2 * G) {
+        const bool isv = gi >= G;
+        const int pg = gi % G;
+        const uint64_t base = isv ? vr : kr, stp = isv ? vstep : kstep;
+        const unsigned dst = tile + (isv ? TILEB : 0u);
+#pragma unroll
+        for (int i = 0; i < CPG; ++i) {
+          const int c = pg + G * i;
+          if (fast) dma16(base + (uint64_t)(16 * i) * stp, goff[sl], dst + (unsigned)(c * RPI * ROWB));
+          else dma16(base, src_off(isv, c, kl), dst + (unsigned)(c * RPI * ROWB));
+        }
       }
     }
   };
@@ -353,7 +364,7 @@ void fwd_bf16_kernel(FwdParams p) {
         lkr = k1;
         lvr = v1;
       }
-      issue_loads(buf, lkr, lvr, JINV, NK);
+      issue_loads(buf, lkr, lvr, true, NK);
       lkr += NK * kstep;
       lvr += NK * vstep;
     } else {
@@ -536,7 +547,7 @@ void fwd_bf16_kernel(FwdParams p) {
     auto step_in = [&](int i, int buf) {
       // my copies of step i are done once at most NBUF-2 later steps'
       // copies are outstanding
-      if (i + NBUF - 2 < nsteps) wait_vmcnt<(NBUF - 2) * LPW>();
+      if (EVEN && i + NBUF - 2 < nsteps) wait_vmcnt<(NBUF - 2) * LPW>();
       else wait_vmem();
       __syncthreads();   // every wave's copies of step i landed; step i-1's buffer is free
       if (lj < nsteps) issue_next((buf + NBUF - 1) % NBUF);
@@ -612,14 +623,9 @@ void fwd_bf16_kernel(FwdParams p) {
   }
 }
 
-// Copies of one K (or V) tile per step: NK rows of 2*D bytes, 1 KB each.
-constexpr int copies_per_tile(int nk16, int D) { return nk16 * 16 * 2 * D / 1024; }
 
 template <int M16, int W, int NK16, int NBUF, int D>
 hipError_t launch_one(const FwdParams &p, const FwdConfig &c, hipStream_t st) {
-  if constexpr (copies_per_tile(NK16, D) % W != 0) {
-    return hipErrorInvalidValue;   // never chosen: choose_fwd_config skips it
-  } else {
   auto kern = fwd_bf16_kernel<M16, W, NK16, NBUF, D>;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
@@ -630,7 +636,6 @@ hipError_t launch_one(const FwdParams &p, const FwdConfig &c, hipStream_t st) {
   if (attr_err != hipSuccess) return attr_err;
   hipLaunchKernelGGL(kern, dim3((unsigned)c.grid), dim3(W * 64), c.lds_bytes, st, p);
   return hipGetLastError();
-  }
 }
 
 }  // namespace
@@ -674,7 +679,6 @@ bool choose_fwd_config(const fsattn_shape *s, const fsattn_mask *m, uint32_t fla
     const int m16 = sh[0], w = sh[1];
     if ((wo && w != wo) || (mo && m16 != mo)) continue;
     if (T % (16 * m16)) continue;
-    if (copies_per_tile(nk16, s->head_dim) % w) continue;
     // keep at least two workgroups per CU within the 160 KB of LDS
     if (2 * fwd_bf16_lds_bytes(nk16, nbuf, s->head_dim) > 160 * 1024) continue;
     const int wave_tiles = T / (16 * m16);

@@ -123,7 +123,7 @@ enum {
                                     instead of bound + scale*q_i.mu */
 };
 /* Optional launch-shape overrides in the flags word (0 = library choice),
- * bf16 inputs only: bits 8..11 waves per workgroup (1, 2, 4 or 8), bits
+ * bf16 inputs only: bits 8..11 waves per workgroup (2, 4 or 8), bits
  * 12..15 query rows per wave divided by 16 (1..4; must divide
  * tokens_per_frame / 16), bits 16..19 keys per pipeline step divided by 16
  * (2 or 4), bits 20..23 K/V staging buffers in the ring (2, 3 or 4; 3 and 4
