@@ -31,7 +31,8 @@ sys.path.insert(0, ROOT)
 METRIC = "live-block attention TFLOP/s and % of bf16 MFMA peak, 1×MI355X"
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
 PEAK_HBM_GBS = 8000.0
-FWD_SOURCES = ["frame_block_sparse_amd/csrc/forward_bf16.hip", "frame_block_sparse_amd/csrc/forward_common.h"]
+FWD_SOURCES = ["frame_block_sparse_amd/csrc/forward_bf16.hip", "frame_block_sparse_amd/csrc/forward_common.h",
+               "frame_block_sparse_amd/csrc/fsattn_internal.h", "frame_block_sparse_amd/csrc/fsattn_schedule.cpp"]
 
 
 def kernel_source_hash() -> str:

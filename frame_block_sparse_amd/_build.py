@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfsattn.so")
 
-SOURCES = ["fsattn_plan.cpp", "fsattn_api.cpp", "plan_device.hip", "bounds_kernels.hip", "forward_f32.hip",
+SOURCES = ["fsattn_plan.cpp", "fsattn_api.cpp", "fsattn_schedule.cpp", "plan_device.hip", "bounds_kernels.hip", "forward_f32.hip",
            "forward_bf16.hip"]
 # per-source extra flags: MFMA accumulators in ordinary VGPRs (the online
 # path rescales them with VALU ops, and it avoids AGPR<->VGPR copies)

@@ -44,9 +44,10 @@
 // constant vmcnt, and one barrier per step publishes them to all waves.
 //
 // Order. Workgroups are issued heavy frames first (frames seeing the most
-// key frames), and the (frame, head) groups are dealt round-robin to the 8
-// XCDs so that all tiles of a group, which stream the same K/V, run on one
-// XCD and share its L2.
+// key frames), and the tiles, in chunks of consecutive tiles of one (frame,
+// head) group, are dealt round-robin to the 8 XCDs, so that tiles that
+// stream the same K/V run on one XCD and share its L2; the chunk size
+// balances the XCDs' work (fsattn_schedule.cpp).
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -68,8 +69,6 @@ typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) unsigned char lds_uchar;
 typedef __attribute__((address_space(1))) void glb_void;
-
-constexpr int kXcds = 8;
 
 __device__ inline f4 mfma32(bf16x8 a, bf16x8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -129,34 +128,23 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Workgroup index -> (frame, batch*head, tile within the frame).
-__device__ inline void map_block(const FwdParams &p, int bid, int &f, int &bh, int &tile) {
+// Workgroup index -> (frame, batch*head, tile within the frame): tile t
+// of XCD x's list (dealt_tile), whose issue-order index g numbers the
+// tiles of (frame, head) group g / TPF, heaviest frames first. Returns false
+// for a workgroup past the end of its XCD's list.
+__device__ inline bool map_block(const FwdParams &p, int bid, int &f, int &bh, int &tile) {
   const int BH = p.B * p.H;
   const int TPF = p.tiles_per_frame;
-  const int NG = p.F * BH;                 // (frame, head) groups
-  const int G = NG * TPF;
-  // the hardware dispatches workgroup ids round-robin over the XCDs; give
-  // each XCD a contiguous range of the logical order
-  const int xcd = bid % kXcds, local = bid / kXcds;
-  const int per = G / kXcds, rem = G % kXcds;
-  const int li = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
-  // logical order: 8 piles, pile q holding groups q, q+8, ... (heavy first)
-  const int A = NG / kXcds, Rg = NG % kXcds;
-  const int big = (A + 1) * TPF;
-  int pile, off;
-  if (li < Rg * big) {
-    pile = li / big;
-    off = li % big;
-  } else {
-    const int l2 = li - Rg * big;
-    pile = Rg + l2 / (A * TPF);
-    off = l2 % (A * TPF);
-  }
-  const int gi = pile + kXcds * (off / TPF);
-  tile = off % TPF;
+  const int64_t G = (int64_t)p.F * BH * TPF;
+  const int x = bid % kXcds, t = bid / kXcds;
+  if (t >= xcd_tile_count(G, p.deal_chunk, x)) return false;
+  const int64_t g = dealt_tile(G, p.deal_chunk, x, t);
+  const int gi = (int)(g / TPF);
+  tile = (int)(g % TPF);
   const int fr = gi / BH;
   bh = gi % BH;
   f = p.ordered ? p.frame_order[fr] : fr;
+  return true;
 }
 
 // Waves per SIMD the register budget is held to: 3 for 32-row waves, 2 for
@@ -194,7 +182,7 @@ void fwd_bf16_kernel(FwdParams p) {
   __builtin_assume(wave >= 0 && wave < W);
   const int g = lane >> 4, n16 = lane & 15;
   int f, bh, ti;
-  map_block(p, blockIdx.x, f, bh, ti);
+  if (!map_block(p, blockIdx.x, f, bh, ti)) return;
   const int b = bh / p.H, h = bh % p.H;
   const int row0 = f * p.T + ti * p.rows_per_wg;
   const bool active = row0 + wave * 16 * M16 < (f + 1) * p.T;   // wave-uniform
@@ -638,6 +626,26 @@ hipError_t launch_one(const FwdParams &p, const FwdConfig &c, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int M16, int W, int NK16, int NBUF, int D>
+int occupancy_one(const FwdConfig &c) {
+  auto kern = fwd_bf16_kernel<M16, W, NK16, NBUF, D>;
+  static std::mutex mu;
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] > 0) return cache[dev];
+  if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          160 * 1024) != hipSuccess)
+    return 0;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void *>(kern), W * 64,
+                                                   c.lds_bytes) != hipSuccess)
+    return 0;
+  cache[dev] = n;
+  return n;
+}
+
 }  // namespace
 
 // (rows per wave / 16, waves per workgroup) pairs built, in order of
@@ -716,6 +724,31 @@ hipError_t launch_forward_bf16(const FwdParams &p, const FwdConfig &c, int head_
   FSATTN_SHAPE_CASE(4, 2)
   FSATTN_SHAPE_CASE(2, 2)
   return hipErrorInvalidValue;
+}
+
+template <int M, int W, int D>
+static int occupancy_steps(const FwdConfig &c) {
+  if (c.nk16 == 2 && c.nbuf == 2) return occupancy_one<M, W, 2, 2, D>(c);
+  if (c.nk16 == 2 && c.nbuf == 3) return occupancy_one<M, W, 2, 3, D>(c);
+  if (c.nk16 == 2 && c.nbuf == 4) return occupancy_one<M, W, 2, 4, D>(c);
+  if (c.nk16 == 4 && c.nbuf == 2) return occupancy_one<M, W, 4, 2, D>(c);
+  return 0;
+}
+
+#define FSATTN_OCC_CASE(M, W)                                                 \
+  if (c.m16 == M && c.waves == W)                                             \
+    return head_dim == 128 ? occupancy_steps<M, W, 128>(c) : occupancy_steps<M, W, 64>(c);
+
+int fwd_bf16_occupancy(const FwdConfig &c, int head_dim) {
+  FSATTN_OCC_CASE(2, 4)
+  FSATTN_OCC_CASE(3, 4)
+  FSATTN_OCC_CASE(1, 4)
+  FSATTN_OCC_CASE(4, 4)
+  FSATTN_OCC_CASE(2, 8)
+  FSATTN_OCC_CASE(3, 2)
+  FSATTN_OCC_CASE(4, 2)
+  FSATTN_OCC_CASE(2, 2)
+  return 0;
 }
 
 }  // namespace fsattn

@@ -130,7 +130,7 @@ extern "C" fsattn_status fsattn_head_bounds(void *hip_stream, const fsattn_shape
 
 namespace {
 
-constexpr uint32_t kKnownFlags = 0x7u | (0xfu << 8) | (0xfu << 12) | (0xfu << 16) | (0xfu << 20);
+constexpr uint32_t kKnownFlags = 0x7u | (0xfu << 8) | (0xfu << 12) | (0xfu << 16) | (0xfu << 20) | (0xfu << 24);
 
 fsattn_status check_forward_host(const fsattn_shape *s, const fsattn_mask *m, uint32_t flags, FwdConfig *cfg) {
   fsattn_status st = check_shape(s, m);
@@ -140,9 +140,11 @@ fsattn_status check_forward_host(const fsattn_shape *s, const fsattn_mask *m, ui
   // the bf16 kernel walks at most two key runs per query frame (window and
   // reference frame), which is all this mask family produces
   if (max_runs_per_frame(m) > (s->dtype == FSATTN_BF16 ? 2 : kMaxRuns)) return FSATTN_ERR_UNSUPPORTED;
-  if (s->dtype == FSATTN_F32 && (flags & (0xfffu << 8))) return FSATTN_ERR_UNSUPPORTED;
+  if (s->dtype == FSATTN_F32 && (flags & (0xfffffu << 8))) return FSATTN_ERR_UNSUPPORTED;
   if (!choose_fwd_config(s, m, flags, cfg)) return FSATTN_ERR_UNSUPPORTED;
   if (cfg->grid / ((int64_t)s->batch * s->heads) > INT32_MAX) return FSATTN_ERR_UNSUPPORTED;
+  // the bf16 grid covers every tile plus at most kXcds - 1 idle ids
+  if (s->dtype == FSATTN_BF16 && cfg->grid > INT32_MAX - kXcds) return FSATTN_ERR_UNSUPPORTED;
   return FSATTN_OK;
 }
 
@@ -203,15 +205,8 @@ extern "C" fsattn_status fsattn_forward(void *hip_stream, const fsattn_shape *s,
   p.flags = flags;
   p.o_f32 = o_dtype == FSATTN_F32 ? 1 : 0;
   // heavy frames (most live key frames) first; ties keep frame order
-  p.ordered = m->num_frames <= kMaxOrderedFrames ? 1 : 0;
-  if (p.ordered) {
-    int n = 0;
-    int64_t most = 0;
-    for (int f = 0; f < m->num_frames; ++f) most = std::max(most, live_frame_count(m, f));
-    for (int64_t c = most; c >= 1 && n < m->num_frames; --c)
-      for (int f = 0; f < m->num_frames; ++f)
-        if (live_frame_count(m, f) == c) p.frame_order[n++] = (uint8_t)f;
-  }
+  p.ordered = frame_issue_order(m, p.frame_order) ? 1 : 0;
+  p.deal_chunk = 1;
   const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   hipError_t e;
   if (s->dtype == FSATTN_F32) {
@@ -221,6 +216,11 @@ extern "C" fsattn_status fsattn_forward(void *hip_stream, const fsattn_shape *s,
   } else {
     p.rows_per_wg = 16 * cfg.m16 * cfg.waves;
     p.tiles_per_frame = (p.T + p.rows_per_wg - 1) / p.rows_per_wg;
+    p.deal_chunk = choose_deal_chunk(s, m, cfg, (int)((flags >> 24) & 15));
+    // XCD x runs ids x, x + kXcds, ...: as many ids per XCD as the longest list
+    int64_t longest = 0;
+    for (int x = 0; x < kXcds; ++x) longest = std::max(longest, xcd_tile_count(cfg.grid, p.deal_chunk, x));
+    cfg.grid = kXcds * longest;
     e = launch_forward_bf16(p, cfg, s->head_dim, stream);
   }
   return e == hipSuccess ? FSATTN_OK : FSATTN_ERR_HIP;

@@ -56,8 +56,31 @@ struct FwdParams {
   // used when num_frames <= kMaxOrderedFrames, natural order otherwise.
   int ordered;
   uint8_t frame_order[64];
+  // Tiles per chunk dealt to one XCD (see dealt_tile).
+  int deal_chunk;
 };
 constexpr int kMaxOrderedFrames = 64;
+
+// The hardware deals workgroup ids round-robin over the XCDs of the device,
+// so XCD x runs ids x, x + kXcds, ... in order.
+constexpr int kXcds = 8;
+
+// The forward's G query tiles in issue order (heaviest frames first, the
+// tiles of one (frame, head) group consecutive) are cut into chunks of C
+// tiles, and the chunks are dealt round-robin to the XCDs; the tiles of a
+// last, partial round are shared out in contiguous ranges. Tile t of XCD x's
+// list is tile dealt_tile(G, C, x, t) of the issue order; the lists' lengths
+// differ by at most one.
+__host__ __device__ inline int64_t xcd_tile_count(int64_t G, int64_t C, int x) {
+  const int64_t A = G / (kXcds * C), Rt = G - kXcds * A * C;
+  return A * C + ((x + 1) * Rt / kXcds - x * Rt / kXcds);
+}
+__host__ __device__ inline int64_t dealt_tile(int64_t G, int64_t C, int x, int64_t t) {
+  const int64_t A = G / (kXcds * C);
+  if (t < A * C) return (kXcds * (t / C) + x) * C + t % C;
+  const int64_t Rt = G - kXcds * A * C;
+  return kXcds * A * C + x * Rt / kXcds + (t - A * C);
+}
 
 struct FwdConfig {
   int waves, m16, nk16, nbuf;   // waves per workgroup, rows per wave / 16, keys per step / 16, ring buffers
@@ -68,6 +91,16 @@ struct FwdConfig {
 // Chooses (or validates an override of) the launch shape; false if none fits.
 bool choose_fwd_config(const fsattn_shape *s, const fsattn_mask *m, uint32_t flags, FwdConfig *cfg);
 hipError_t launch_forward_bf16(const FwdParams &p, const FwdConfig &c, int head_dim, hipStream_t st);
+// Workgroups of this launch shape resident per CU on the current device (0
+// if unknown).
+int fwd_bf16_occupancy(const FwdConfig &c, int head_dim);
+// Issue order of the query frames, heaviest first (fsattn_schedule.cpp);
+// false when the natural order is used (more than kMaxOrderedFrames frames).
+bool frame_issue_order(const fsattn_mask *m, uint8_t *order);
+// Chunk size of the dealing (fsattn_schedule.cpp): `override` 0 picks it
+// from a model of the per-XCD dispatch on the current device, 1..14 give
+// 2^(override-1) tiles, 15 whole (frame, head) groups. Host only.
+int choose_deal_chunk(const fsattn_shape *s, const fsattn_mask *m, const FwdConfig &c, int override);
 hipError_t launch_forward_f32(const FwdParams &p, int head_dim, hipStream_t st);
 int f32_rows_per_wg(int T);
 

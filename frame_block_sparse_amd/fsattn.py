@@ -256,7 +256,9 @@ _MODES = {"auto": MODE_AUTO, "online": MODE_FORCE_ONLINE, "fixed": MODE_FORCE_FI
 
 
 def make_flags(mode: str = "auto", per_row_shift: bool = False, waves: int = 0, rows_per_wave: int = 0,
-               key_step: int = 0, ring: int = 0) -> int:
+               key_step: int = 0, ring: int = 0, deal: int = 0) -> int:
+    """Flags word of fsattn_forward (see include/fsattn.h). deal: 0 library
+    choice, 1..14 chunks of 2**(deal-1) tiles, 15 whole (frame, head) groups."""
     f = _MODES[mode]
     if per_row_shift:
         f |= SHIFT_PER_ROW
@@ -264,6 +266,7 @@ def make_flags(mode: str = "auto", per_row_shift: bool = False, waves: int = 0, 
     f |= ((rows_per_wave // 16) & 15) << 12
     f |= ((key_step // 16) & 15) << 16
     f |= (ring & 15) << 20
+    f |= (deal & 15) << 24
     return f
 
 

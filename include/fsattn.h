@@ -14,8 +14,9 @@
  *
  * Conventions shared by every call:
  *  - Ownership: the caller owns every buffer, host or device. The library
- *    never allocates device memory, never synchronises a stream and keeps
- *    no mutable global state.
+ *    never allocates device memory and never synchronises a stream. Its
+ *    only global state is a cache of launch choices per device and
+ *    geometry (thread-safe).
  *  - Errors: arguments are validated on the host before any launch. On any
  *    error nothing is launched and no output is written. A failed launch is
  *    reported as FSATTN_ERR_HIP. Device faults surface on the stream.
@@ -133,6 +134,11 @@ enum {
 #define FSATTN_FLAG_ROWS16(m) ((uint32_t)(m) << 12)
 #define FSATTN_FLAG_KSTEP16(s) ((uint32_t)(s) << 16)
 #define FSATTN_FLAG_RING(b) ((uint32_t)(b) << 20)
+/* How the query tiles are dealt to the XCDs, bits 24..27 (bf16 inputs
+ * only): 0 = library choice, 1..14 = chunks of 2^(v-1) consecutive tiles
+ * of one (frame, head) group, 15 = whole groups. The results do not depend
+ * on it (every tile is computed the same way wherever it runs). */
+#define FSATTN_FLAG_DEAL(v) ((uint32_t)(v) << 24)
 
 #define FSATTN_DEFAULT_GAP_NATS 30.0f
 
@@ -219,9 +225,10 @@ fsattn_status fsattn_forward(void *hip_stream, const fsattn_shape *s, const fsat
 
 /*
  * Launch shape fsattn_forward would use for these arguments (host only):
- * waves per workgroup, query rows per wave, keys per pipeline step,
- * workgroups in the grid and dynamic LDS bytes per workgroup. Any output
- * pointer may be NULL. Errors: as fsattn_forward's host validation.
+ * waves per workgroup, query rows per wave, keys per pipeline step, query
+ * tiles (one workgroup each; the bf16 grid adds up to 7 idle ids so that
+ * every XCD gets whole rounds) and dynamic LDS bytes per workgroup. Any
+ * output pointer may be NULL. Errors: as fsattn_forward's host validation.
  */
 fsattn_status fsattn_forward_launch_info(const fsattn_shape *s, const fsattn_mask *m, uint32_t flags,
                                          int32_t *waves, int32_t *rows_per_wave, int32_t *key_step,

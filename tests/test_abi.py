@@ -156,7 +156,8 @@ def test_forward_validation():
     assert _fwd_call(shape=F.Shape(1, 2, 240, 128, 3)) == 3
     assert _fwd_call(mask=F.to_mask((5, 48, 1, 1, 0, 48, 32))) == 2
     assert _fwd_call(flags=3) == 1                                             # both modes
-    assert _fwd_call(flags=1 << 24) == 1                                       # unknown bit
+    assert _fwd_call(flags=1 << 28) == 1                                       # unknown bit
+    assert _fwd_call(flags=fs.make_flags(deal=3)) == 3                         # fp32 path has no dealing
     assert _fwd_call(km=None) == 1                                             # fixed path needs the record
     assert _fwd_call(rp=None) == 1
     assert _fwd_call(ci=None) == 1

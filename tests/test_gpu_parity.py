@@ -185,6 +185,24 @@ def test_forward_small_parity(dev, case, mode):
     assert lerr <= LSE_TOL[w.dtype], lerr
 
 
+@pytest.mark.parametrize("i", [2, 5])
+def test_forward_dealing_is_bitwise_neutral(dev, config_inputs, i):
+    """How the tiles are dealt to the XCDs (whole (frame, head) groups, the
+    library's chunks, single tiles, a chunk larger than a group) changes only
+    where each tile runs: the outputs are bitwise equal."""
+    w = workloads.config(i)
+    q, k, v = config_inputs(i)
+    qd, kd, vd = (_to_dev(x, torch.bfloat16, dev) for x in (q, k, v))
+    dp = fs.device_plan(w, dev)
+    bnd = fs.head_bounds(qd, kd, w)
+    ref = fs.forward(qd, kd, vd, dp, bnd, flags=fs.make_flags(deal=15))
+    for deal in (0, 1, 3, 9):
+        _say(f"[deal] workload {i} deal={deal}")
+        out = fs.forward(qd, kd, vd, dp, bnd, flags=fs.make_flags(deal=deal))
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), deal
+
+
 _SHAPE_REF = {}
 
 
