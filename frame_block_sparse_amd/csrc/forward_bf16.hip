@@ -186,7 +186,6 @@ void fwd_bf16_kernel(FwdParams p) {
   const int b = bh / p.H, h = bh % p.H;
   const int row0 = f * p.T + ti * p.rows_per_wg;
   const bool active = row0 + wave * 16 * M16 < (f + 1) * p.T;   // wave-uniform
-  if (wave == 0) build_runs(p.row_ptr, p.col_idx, p.nnz, row0 / p.bq, p.bk, p.N, runs, nruns_sm);
 
   const __bf16 *qb = static_cast<const __bf16 *>(p.q) + b * p.qsb + h * p.qsh;
   // K and V bases of this (batch, head) as wave-uniform byte addresses: the
@@ -195,8 +194,11 @@ void fwd_bf16_kernel(FwdParams p) {
   const uint64_t vb = uniform_ptr(static_cast<const __bf16 *>(p.v) + b * p.vsb + h * p.vsh);
   const int wrow0 = row0 + wave * 16 * M16;
 
-  // Q fragments (B operand of S^T = K Q^T): row n16 of each 16-row group,
-  // d = 32*kd + 8*g .. +7.
+  // Prologue loads, issued together so that their latencies overlap (and
+  // overlap the plan reads of wave 0 and the first K/V copies below): the Q
+  // fragments (B operand of S^T = K Q^T: row n16 of each 16-row group,
+  // d = 32*kd + 8*g .. +7) and, unless every head runs online, the head's
+  // record and this lane's slices of its mean key.
   // An idle wave reads its workgroup's first rows instead (always in range)
   // and never stores.
   const int qrow0 = active ? wrow0 : row0;
@@ -207,38 +209,24 @@ void fwd_bf16_kernel(FwdParams p) {
     for (int kd = 0; kd < KD; ++kd)
       qf[m][kd] = *reinterpret_cast<const bf16x8 *>(qb + (int64_t)(qrow0 + 16 * m + n16) * p.qsn +
                                                      32 * kd + 8 * g);
-  wait_vmem();
-
   const int mode = p.flags & 3;
-  const bool fixed = mode == FSATTN_MODE_FORCE_FIXED ||
-                     (mode == FSATTN_MODE_AUTO && p.rec[bh].eligible != 0);
-  float sh[M16];   // fixed: the row's shift; online: the running max (log2 units)
-  if (fixed) {
-    const float *mu = p.key_mean + (int64_t)bh * D;
-    const float bound = p.rec[bh].bound, kmax = p.rec[bh].k_norm_max;
-    const bool per_row = (p.flags & FSATTN_SHIFT_PER_ROW) != 0;
+  const bool may_fix = mode != FSATTN_MODE_FORCE_ONLINE;   // key_mean and rec are given
+  int eligible = 0;
+  float bound = 0.f, kmax = 0.f;
+  float4 muv[KD][2];
+  if (may_fix) {
+    eligible = p.rec[bh].eligible;
+    bound = p.rec[bh].bound;
+    kmax = p.rec[bh].k_norm_max;
+    const float4 *mu4 = reinterpret_cast<const float4 *>(p.key_mean + (int64_t)bh * D + 8 * g);
 #pragma unroll
-    for (int m = 0; m < M16; ++m) {
-      float dot = 0.f, nq = 0.f;
-#pragma unroll
-      for (int kd = 0; kd < KD; ++kd)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const float x = (float)qf[m][kd][t];
-          dot = fmaf(x, mu[32 * kd + 8 * g + t], dot);
-          nq = fmaf(x, x, nq);
-        }
-      dot += __shfl_xor(dot, 16);
-      dot += __shfl_xor(dot, 32);
-      nq += __shfl_xor(nq, 16);
-      nq += __shfl_xor(nq, 32);
-      const float mrow = per_row ? p.scale * (sqrtf(nq) * kmax + dot) : bound + p.scale * dot;
-      sh[m] = mrow * kLog2e;
+    for (int kd = 0; kd < KD; ++kd) {
+      muv[kd][0] = mu4[8 * kd];
+      muv[kd][1] = mu4[8 * kd + 1];
     }
-  } else {
-#pragma unroll
-    for (int m = 0; m < M16; ++m) sh[m] = -INFINITY;
   }
+  if (wave == 0) build_runs(p.row_ptr, p.col_idx, p.nnz, row0 / p.bq, p.bk, p.N, runs, nruns_sm);
+
   float lsum[M16];
   f4 oacc[M16][DT];
 #pragma unroll
@@ -362,6 +350,46 @@ void fwd_bf16_kernel(FwdParams p) {
     }
     ++lj;
   };
+
+  // The ring's first NBUF-1 steps go out now, so the shift computation
+  // below (which waits for the prologue loads) runs while they are in flight.
+#pragma unroll
+  for (int j = 0; j < NBUF - 1; ++j)
+    if (lj < nsteps) issue_next(j);
+
+  const bool fixed = mode == FSATTN_MODE_FORCE_FIXED || (mode == FSATTN_MODE_AUTO && eligible != 0);
+  float sh[M16];   // fixed: the row's shift; online: the running max (log2 units)
+  if (fixed) {
+    const bool per_row = (p.flags & FSATTN_SHIFT_PER_ROW) != 0;
+#pragma unroll
+    for (int m = 0; m < M16; ++m) {
+      float dot = 0.f, nq = 0.f;
+#pragma unroll
+      for (int kd = 0; kd < KD; ++kd)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float x = (float)qf[m][kd][t];
+          const float4 mv = muv[kd][t >> 2];
+          const float mu = (t & 3) == 0 ? mv.x : (t & 3) == 1 ? mv.y : (t & 3) == 2 ? mv.z : mv.w;
+          dot = fmaf(x, mu, dot);
+          nq = fmaf(x, x, nq);
+        }
+      dot += __shfl_xor(dot, 16);
+      dot += __shfl_xor(dot, 32);
+      nq += __shfl_xor(nq, 16);
+      nq += __shfl_xor(nq, 32);
+      const float mrow = per_row ? p.scale * (sqrtf(nq) * kmax + dot) : bound + p.scale * dot;
+      sh[m] = mrow * kLog2e;
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < M16; ++m) sh[m] = -INFINITY;
+  }
+  // Every prologue load is complete after this (it is also step 0's wait
+  // with a two-buffer ring), so the compiler has no load of its own left to
+  // wait for inside the step loop, where the wait would also cover the
+  // prefetch.
+  wait_vmem();
 
   // Per-lane LDS addresses of the MFMA operand reads in a tile at offset 0
   // of the ring whose first row is a multiple of 16 (both swizzles have
@@ -528,9 +556,6 @@ void fwd_bf16_kernel(FwdParams p) {
   // that folds into the LDS instructions.
   auto main_loop = [&](auto fixed_tag, auto compute_tag) {
     constexpr bool COMPUTE = decltype(compute_tag)::value;
-#pragma unroll
-    for (int j = 0; j < NBUF - 1; ++j)
-      if (lj < nsteps) issue_next(j);
     // step i's copies in: wait, publish, refill the buffer step i-1 used
     auto step_in = [&](int i, int buf) {
       // my copies of step i are done once at most NBUF-2 later steps'

@@ -189,6 +189,7 @@ extern "C" fsattn_status fsattn_forward(void *hip_stream, const fsattn_shape *s,
   if (nnz != want_nnz) return FSATTN_ERR_INVALID_ARGUMENT;
   const int mode = flags & 3;
   if (mode != FSATTN_MODE_FORCE_ONLINE && (!key_mean || !rec)) return FSATTN_ERR_INVALID_ARGUMENT;
+  if (key_mean && reinterpret_cast<uintptr_t>(key_mean) % 16) return FSATTN_ERR_INVALID_ARGUMENT;
   if (!(scale > 0.f) || !std::isfinite(scale)) return FSATTN_ERR_INVALID_ARGUMENT;
 
   FwdParams p;

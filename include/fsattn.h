@@ -210,7 +210,7 @@ fsattn_status fsattn_head_bounds(void *hip_stream, const fsattn_shape *s, const 
  * (nnz entries); the kernel relies on all query blocks of a frame sharing
  * one list, which fsattn_plan guarantees. key_mean/rec: fsattn_head_bounds'
  * output for the same Q/K and scale (needed by the fixed path; may be NULL
- * only with FSATTN_MODE_FORCE_ONLINE). o: output [B,H,N,d] of o_dtype
+ * only with FSATTN_MODE_FORCE_ONLINE; key_mean 16-byte aligned). o: output [B,H,N,d] of o_dtype
  * (the input dtype, or FSATTN_F32). lse: optional device [B*H*N] fp32
  * log-sum-exp (natural log) per row, or NULL. Asynchronous on hip_stream;
  * deterministic (no atomics).
