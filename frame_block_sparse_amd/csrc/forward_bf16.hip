@@ -227,11 +227,17 @@ void fwd_bf16_kernel(FwdParams p) {
   }
   if (wave == 0) build_runs(p.row_ptr, p.col_idx, p.nnz, row0 / p.bq, p.bk, p.N, runs, nruns_sm);
 
+  // Row sums: the online path adds the probabilities with v_dot2c (it
+  // rescales the sum with one multiply); the fixed path sums them on the
+  // matrix unit, as O's column tile of an all-ones V, which every lane of a
+  // row then holds whole (4 copies).
   float lsum[M16];
+  f4 lsum4[M16];
   f4 oacc[M16][DT];
 #pragma unroll
   for (int m = 0; m < M16; ++m) {
     lsum[m] = 0.f;
+    lsum4[m] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[m][dt] = f4{0.f, 0.f, 0.f, 0.f};
   }
@@ -503,23 +509,33 @@ void fwd_bf16_kernel(FwdParams p) {
       for (int t = 0; t < NS; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[m][t][i] = __builtin_amdgcn_exp2f(fmaf(s[m][t][i], c2, nsh));
-      // the row sum adds the probabilities PV multiplies (bf16), a pair per
-      // v_dot2c_f32_bf16
+      // the row sum adds the probabilities PV multiplies (bf16)
       if constexpr (NS == 2) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           pk[m][i] = (__bf16)s[m][0][i];
           pk[m][4 + i] = (__bf16)s[m][1][i];
         }
-        const u4 w = __builtin_bit_cast(u4, pk[m]);
+        if constexpr (FIXED) {
+          const bf16x8 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                               (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+          lsum4[m] = mfma32(ones, pk[m], lsum4[m]);
+        } else {
+          const u4 w = __builtin_bit_cast(u4, pk[m]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) lsum[m] = add_bf16_pair(lsum[m], w[j]);
+          for (int j = 0; j < 4; ++j) lsum[m] = add_bf16_pair(lsum[m], w[j]);
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) pt[m][i] = (__bf16)s[m][0][i];
-        const u2 w = __builtin_bit_cast(u2, pt[m]);
+        if constexpr (FIXED) {
+          const bf16x4 ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+          lsum4[m] = mfma16(ones, pt[m], lsum4[m]);
+        } else {
+          const u2 w = __builtin_bit_cast(u2, pt[m]);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) lsum[m] = add_bf16_pair(lsum[m], w[j]);
+          for (int j = 0; j < 2; ++j) lsum[m] = add_bf16_pair(lsum[m], w[j]);
+        }
       }
     }
     if constexpr (VPF) {
@@ -606,12 +622,18 @@ void fwd_bf16_kernel(FwdParams p) {
   else
     main_loop(std::false_type{}, std::true_type{});
 
-  // Epilogue: one cross-lane reduction of the row sums, normalise, store.
+  // Epilogue: the row sums (one cross-lane reduction on the online path),
+  // normalise, store.
 #pragma unroll
   for (int m = 0; m < M16; ++m) {
-    float l = lsum[m];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    float l;
+    if (fixed) {
+      l = lsum4[m][0];
+    } else {
+      l = lsum[m];
+      l += __shfl_xor(l, 16);
+      l += __shfl_xor(l, 32);
+    }
     const float inv = 1.f / l;
     const int row = wrow0 + 16 * m + n16;
     if (p.o_f32) {
