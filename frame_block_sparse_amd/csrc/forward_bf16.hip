@@ -185,7 +185,11 @@ void fwd_bf16_kernel(FwdParams p) {
   if (!map_block(p, blockIdx.x, f, bh, ti)) return;
   const int b = bh / p.H, h = bh % p.H;
   const int row0 = f * p.T + ti * p.rows_per_wg;
-  const bool active = row0 + wave * 16 * M16 < (f + 1) * p.T;   // wave-uniform
+  const int fend = (f + 1) * p.T;   // the frame's end row
+  // A wave whose 16 * M16 rows run past the frame's end (when they do not
+  // divide the frame span) computes its rows past the end on the frame's
+  // last query row and does not store them.
+  const bool active = row0 + wave * 16 * M16 < fend;   // wave-uniform
 
   const __bf16 *qb = static_cast<const __bf16 *>(p.q) + b * p.qsb + h * p.qsh;
   // K and V bases of this (batch, head) as wave-uniform byte addresses: the
@@ -207,7 +211,7 @@ void fwd_bf16_kernel(FwdParams p) {
   for (int m = 0; m < M16; ++m)
 #pragma unroll
     for (int kd = 0; kd < KD; ++kd)
-      qf[m][kd] = *reinterpret_cast<const bf16x8 *>(qb + (int64_t)(qrow0 + 16 * m + n16) * p.qsn +
+      qf[m][kd] = *reinterpret_cast<const bf16x8 *>(qb + (int64_t)min(qrow0 + 16 * m + n16, fend - 1) * p.qsn +
                                                      32 * kd + 8 * g);
   const int mode = p.flags & 3;
   const bool may_fix = mode != FSATTN_MODE_FORCE_ONLINE;   // key_mean and rec are given
@@ -636,6 +640,7 @@ void fwd_bf16_kernel(FwdParams p) {
     }
     const float inv = 1.f / l;
     const int row = wrow0 + 16 * m + n16;
+    if (row >= fend) continue;
     if (p.o_f32) {
       float *orow = static_cast<float *>(p.o) + b * p.osb + h * p.osh + (int64_t)row * p.osn;
 #pragma unroll
@@ -733,10 +738,13 @@ bool choose_fwd_config(const fsattn_shape *s, const fsattn_mask *m, uint32_t fla
   for (const auto &sh : kShapes) {
     const int m16 = sh[0], w = sh[1];
     if ((wo && w != wo) || (mo && m16 != mo)) continue;
-    if (T % (16 * m16)) continue;
+    // the library's choice takes wave tiles that divide the frame span; an
+    // explicit rows-per-wave override may leave a frame's last wave partly
+    // past its end
+    if (!mo && T % (16 * m16)) continue;
     // keep at least two workgroups per CU within the 160 KB of LDS
     if (2 * fwd_bf16_lds_bytes(nk16, nbuf, s->head_dim) > 160 * 1024) continue;
-    const int wave_tiles = T / (16 * m16);
+    const int wave_tiles = (T + 16 * m16 - 1) / (16 * m16);
     cfg->waves = w;
     cfg->m16 = m16;
     cfg->nk16 = nk16;

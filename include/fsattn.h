@@ -125,10 +125,12 @@ enum {
 };
 /* Optional launch-shape overrides in the flags word (0 = library choice),
  * bf16 inputs only: bits 8..11 waves per workgroup (2, 4 or 8), bits
- * 12..15 query rows per wave divided by 16 (1..4; must divide
- * tokens_per_frame / 16), bits 16..19 keys per pipeline step divided by 16
- * (2 or 4), bits 20..23 K/V staging buffers in the ring (2, 3 or 4; 3 and 4
- * with 32-key steps only). An override that is not built or does not fit
+ * 12..15 query rows per wave divided by 16 (1..4; the library's own
+ * choice divides tokens_per_frame, an explicit one need not: a frame's
+ * last wave then also computes rows past the frame's end, on the frame's
+ * last query row, and stores only its live rows), bits 16..19 keys per
+ * pipeline step divided by 16 (2 or 4), bits 20..23 K/V staging buffers in
+ * the ring (2, 3 or 4; 3 and 4 with 32-key steps only). An override that is not built or does not fit
  * the geometry returns FSATTN_ERR_UNSUPPORTED. */
 #define FSATTN_FLAG_WAVES(n) ((uint32_t)(n) << 8)
 #define FSATTN_FLAG_ROWS16(m) ((uint32_t)(m) << 12)

@@ -176,9 +176,10 @@ def test_launch_info_choices():
         assert wgs == w.batch * w.heads * w.num_frames * tiles
         assert lds <= 160 * 1024
     w = workloads.config(3)
-    with pytest.raises(fs.FsattnError) as e:      # 64-row wave tiles do not divide 3600
-        fs.launch_info((1, 5, 32400, 128), fs.BF16, w, fs.make_flags(waves=4, rows_per_wave=64))
-    assert e.value.status == 3
+    # an explicit rows-per-wave that does not divide the frame span (3600 = 56 * 64 + 16) is
+    # accepted: a frame's last wave runs partly past the frame's end and stores only its live rows
+    waves, rows, _, wgs, _ = fs.launch_info((1, 5, 32400, 128), fs.BF16, w, fs.make_flags(waves=4, rows_per_wave=64))
+    assert (waves, rows) == (4, 64) and wgs == 5 * 9 * 15
     waves, rows, _, _, _ = fs.launch_info((1, 5, 32400, 128), fs.BF16, w, fs.make_flags(waves=2, rows_per_wave=48))
     assert (waves, rows) == (2, 48)
     with pytest.raises(fs.FsattnError):           # 5-wave workgroups are not built

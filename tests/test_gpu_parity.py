@@ -226,6 +226,42 @@ def test_forward_launch_shapes(dev, shape):
         assert err <= TOL["bf16"], (mode, err)
 
 
+RAGGED = [(4, 32, 48), (4, 32, 80), (2, 32, 112), (4, 48, 80), (4, 64, 48), (4, 64, 112), (8, 32, 208),
+          (2, 64, 16)]
+
+
+@pytest.mark.parametrize("shape", RAGGED, ids=[f"w{a}_r{b}_T{c}" for a, b, c in RAGGED])
+def test_forward_ragged_last_wave(dev, shape):
+    """Rows per wave that do not divide the frame span: each frame's last wave
+    runs partly past the frame's end (in the last frame, past the sequence's
+    end), computes those rows on the frame's last query row and stores only
+    its live rows. Every row matches the oracle, on both softmax paths, and a
+    sentinel in the output shows nothing outside the live rows is written."""
+    waves, rows, T = shape
+    case = (f"ragged{T}", 2, 2, 4, T, 128, "bf16", 1, 1, 0, 16, 16)
+    w, q, k, v = _small(case, seed=6, key_offset=0.25)
+    ref, ref_lse = oracle.attention_ref(q, k, v, _geom(w))
+    qd, kd, vd = (_to_dev(x, torch.bfloat16, dev) for x in (q, k, v))
+    dp = fs.device_plan(w, dev)
+    bnd = fs.head_bounds(qd, kd, w)
+    for mode in ("auto", "online"):
+        _say(f"[fwd-ragged] waves={waves} rows={rows} T={T} mode={mode}")
+        flags = fs.make_flags(mode, waves=waves, rows_per_wave=rows)
+        assert fs.launch_info(tuple(qd.shape), fs.BF16, w, flags)[:2] == (waves, rows)
+        # one extra row on each side of the output and LSE, holding a sentinel
+        big = torch.full((w.batch, w.heads, w.seq_len + 2, w.head_dim), 7.0, dtype=torch.bfloat16, device=dev)
+        lse_big = torch.full((w.batch * w.heads * w.seq_len + 2,), 7.0, dtype=torch.float32, device=dev)
+        out = big[:, :, 1:w.seq_len + 1]
+        lse = lse_big[1:-1].view(w.batch, w.heads, w.seq_len)
+        fs.forward(qd, kd, vd, dp, bnd, flags=flags, out=out, lse=lse)
+        torch.cuda.synchronize()
+        err = np.abs(out.float().cpu().numpy() - ref).max()
+        assert err <= TOL["bf16"], (mode, err)
+        assert np.abs(lse.cpu().numpy() - ref_lse).max() <= LSE_TOL["bf16"], mode
+        assert (big[:, :, 0] == 7.0).all() and (big[:, :, -1] == 7.0).all()
+        assert lse_big[0].item() == 7.0 and lse_big[-1].item() == 7.0
+
+
 def test_forward_fp32_output_and_strided_layout(dev):
     case = ("strided", 2, 3, 4, 144, 128, "bf16", 1, 1, 0, 48, 48)
     w, q, k, v = _small(case, seed=3)
