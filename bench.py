@@ -63,6 +63,55 @@ def read_traffic(workload: str):
         return None
 
 
+def partial_tile_share(w, tile: int = 128):
+    """How many tile x tile blocks of the attention matrix (sequence padded to
+    a multiple of `tile`) would be live and how many of those only partly
+    live under this frame mask: the cost the frame-aligned blocks avoid."""
+    import numpy as np
+    F_, T, N = w.num_frames, w.tokens_per_frame, w.seq_len
+    live = np.zeros((F_, F_), dtype=np.int64)   # live[f, g]: key frame g is visible from query frame f
+    for f in range(F_):
+        live[f, max(0, f - w.window_before):min(F_ - 1, f + w.window_after) + 1] = 1
+        if w.ref_frame >= 0:
+            live[f, w.ref_frame] = 1
+    pre = np.zeros((F_ + 1, F_ + 1), dtype=np.int64)
+    pre[1:, 1:] = live.cumsum(0).cumsum(1)
+    nt = -(-N // tile)
+    lo = np.arange(nt) * tile
+    hi = np.minimum(lo + tile, N) - 1            # last real token of each tile
+    padded = lo + tile > N
+    fa, fb = lo // T, hi // T                     # frames a tile spans
+    cnt = (pre[fb[:, None] + 1, fb[None, :] + 1] - pre[fa[:, None], fb[None, :] + 1]
+           - pre[fb[:, None] + 1, fa[None, :]] + pre[fa[:, None], fa[None, :]])
+    span = (fb - fa + 1)[:, None] * (fb - fa + 1)[None, :]
+    any_live = cnt > 0
+    # every (query, key) pair live: all frame pairs live and no padding
+    all_live = (cnt == span) & ~padded[:, None] & ~padded[None, :]
+    n_live, n_partial = int(any_live.sum()), int((any_live & ~all_live).sum())
+    return {"tile": tile, "live_tiles": n_live, "partial_tiles": n_partial,
+            "partial_frac": round(n_partial / n_live, 4) if n_live else 0.0}
+
+
+def mfma_reference(dev, reps: int = 5):
+    """The pure-MFMA reference loop (fsattn_mfma_probe): 8 waves per CU,
+    timed with events; TFLOP/s at the clock the device holds under it."""
+    import torch
+    import frame_block_sparse_amd as fs
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    wgs, iters = 2 * cus, 20000
+    fs.mfma_probe(wgs, iters, dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    flops = 0
+    for a, b in ev:
+        a.record()
+        flops = fs.mfma_probe(wgs, iters, dev)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+    return {"kernel": "mfma_probe_kernel", "workgroups": wgs, "iters": iters,
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+
+
 def cpu_baseline(w, q, k, v, budget_s: float):
     """fp64 oracle on a bounded sample of query rows (every frame, every
     head), timed on the host cores. Rate in live TFLOP/s."""
@@ -216,6 +265,7 @@ def main():
     bnd_ms = [b.elapsed_time(c) for _, b, c in aux]
     bnd_avg = sum(bnd_ms) / len(bnd_ms)
     achieved = live_flops / (fwd_avg * 1e-3) / 1e12
+    ref_mfma = mfma_reference(dev) if w.dtype == "bf16" else None
     value = live_flops / (ms_step * 1e-3) / 1e12
     elig = bnd.host()["eligible"]
     esz = 2 if w.dtype == "bf16" else 4
@@ -250,7 +300,10 @@ def main():
             "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": read_traffic(w.name),
             "avg_launch_ms": round(fwd_avg, 5), "algorithmic_flop_per_launch": live_flops,
+            "measured_mfma_peak": ref_mfma,
+            "frac_of_measured_peak": round(achieved / ref_mfma["tflops"], 4) if ref_mfma else None,
         },
+        "partial_tiles_if_128": partial_tile_share(w),
         "plan": {"avg_ms": round(sum(plan_ms) / len(plan_ms), 5), "nnz": nnz},
         "bounds": {"avg_ms": round(bnd_avg, 5), "algorithmic_bytes": bounds_bytes,
                    "GBps": round(bounds_bytes / (bnd_avg * 1e-3) / 1e9, 1), "peak_GBps": PEAK_HBM_GBS},

@@ -18,10 +18,10 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfsattn.so")
 
 SOURCES = ["fsattn_plan.cpp", "fsattn_api.cpp", "fsattn_schedule.cpp", "plan_device.hip", "bounds_kernels.hip", "forward_f32.hip",
-           "forward_bf16.hip"]
+           "forward_bf16.hip", "mfma_probe.hip"]
 # per-source extra flags: MFMA accumulators in ordinary VGPRs (the online
 # path rescales them with VALU ops, and it avoids AGPR<->VGPR copies)
-EXTRA = {"forward_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"forward_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "mfma_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -226,3 +226,11 @@ extern "C" fsattn_status fsattn_forward(void *hip_stream, const fsattn_shape *s,
   }
   return e == hipSuccess ? FSATTN_OK : FSATTN_ERR_HIP;
 }
+
+extern "C" fsattn_status fsattn_mfma_probe(void *hip_stream, int32_t workgroups, int32_t iters, float *sink,
+                                           int64_t *flops) {
+  if (workgroups < 1 || workgroups > (1 << 20) || iters < 1 || !sink) return FSATTN_ERR_INVALID_ARGUMENT;
+  if (flops) *flops = mfma_probe_flops(workgroups, iters);
+  const hipError_t e = launch_mfma_probe(workgroups, iters, sink, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? FSATTN_OK : FSATTN_ERR_HIP;
+}

@@ -102,6 +102,9 @@ bool frame_issue_order(const fsattn_mask *m, uint8_t *order);
 // 2^(override-1) tiles, 15 whole (frame, head) groups. Host only.
 int choose_deal_chunk(const fsattn_shape *s, const fsattn_mask *m, const FwdConfig &c, int override);
 hipError_t launch_forward_f32(const FwdParams &p, int head_dim, hipStream_t st);
+// Pure-MFMA reference loop (mfma_probe.hip) and the FLOPs one launch does.
+hipError_t launch_mfma_probe(int workgroups, int iters, float *sink, hipStream_t st);
+int64_t mfma_probe_flops(int workgroups, int iters);
 int f32_rows_per_wg(int T);
 
 }  // namespace fsattn

@@ -84,11 +84,12 @@ def lib() -> ctypes.CDLL:
                                  ctypes.c_void_p, ctypes.c_float, ctypes.c_uint32, ctypes.c_void_p]
     L.fsattn_forward_launch_info.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Mask), ctypes.c_uint32,
                                              c_i32p, c_i32p, c_i32p, c_i64p, c_i32p]
+    L.fsattn_mfma_probe.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, c_i64p]
     L.fsattn_status_string.argtypes = [ctypes.c_int]
     L.fsattn_status_string.restype = ctypes.c_char_p
     L.fsattn_abi_version.argtypes = []
     for name in ("fsattn_plan_size", "fsattn_plan", "fsattn_plan_device", "fsattn_head_bounds", "fsattn_forward",
-                 "fsattn_forward_launch_info"):
+                 "fsattn_forward_launch_info", "fsattn_mfma_probe"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -303,3 +304,15 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dplan: DevicePlan
                                 km, rc, float(scale), int(flags),
                                 lse.data_ptr() if lse is not None else None), "fsattn_forward")
     return out
+
+
+def mfma_probe(workgroups: int, iters: int, device=None, stream: Optional[int] = None) -> int:
+    """Launches the pure-MFMA reference loop (fsattn_mfma_probe) on the
+    current stream and returns the FLOPs it performs; time it with events."""
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    sink = torch.empty(max(1, workgroups), dtype=torch.float32, device=dev)
+    flops = ctypes.c_int64()
+    _check(lib().fsattn_mfma_probe(stream if stream is not None else torch.cuda.current_stream(dev).cuda_stream,
+                                   int(workgroups), int(iters), sink.data_ptr(), ctypes.byref(flops)),
+           "fsattn_mfma_probe")
+    return flops.value

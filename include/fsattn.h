@@ -236,6 +236,21 @@ fsattn_status fsattn_forward_launch_info(const fsattn_shape *s, const fsattn_mas
                                          int32_t *waves, int32_t *rows_per_wave, int32_t *key_step,
                                          int64_t *workgroups, int32_t *lds_bytes);
 
+/*
+ * Measurement aid (not part of the attention path): a reference rate for
+ * the matrix unit. Launches `workgroups` workgroups of 4 waves that each
+ * run `iters` rounds of 8 independent v_mfma_f32_16x16x32_bf16 (the forward
+ * kernel's instruction) on register operands, with no memory traffic, and
+ * write one float per workgroup to sink (DEVICE memory, >= workgroups
+ * floats; the values carry no meaning). *flops (host, may be NULL)
+ * receives the launch's multiply-add count x 2. Timing the launch on the
+ * stream gives the bf16 MFMA rate the device reaches at the clock it holds
+ * under a pure matrix load. Errors: INVALID_ARGUMENT (workgroups outside
+ * [1, 2^20], iters < 1, NULL sink), HIP.
+ */
+fsattn_status fsattn_mfma_probe(void *hip_stream, int32_t workgroups, int32_t iters, float *sink,
+                                int64_t *flops);
+
 /* Static description of a status code. */
 const char *fsattn_status_string(fsattn_status st);
 

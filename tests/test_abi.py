@@ -199,3 +199,12 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(F, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="not built"):
         F.lib()
+
+
+def test_mfma_probe_validates_on_host():
+    L = fs.lib()
+    flops = ctypes.c_int64()
+    assert L.fsattn_mfma_probe(None, 0, 10, FAKE, ctypes.byref(flops)) == 1
+    assert L.fsattn_mfma_probe(None, 1 << 21, 10, FAKE, ctypes.byref(flops)) == 1
+    assert L.fsattn_mfma_probe(None, 4, 0, FAKE, ctypes.byref(flops)) == 1
+    assert L.fsattn_mfma_probe(None, 4, 10, None, ctypes.byref(flops)) == 1

@@ -349,3 +349,20 @@ def test_forward_deterministic(dev, config_inputs):
     d = fs.forward(qd, kd, vd, dp, bnd, flags=fs.make_flags("online"))
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(c, d)
+
+
+def test_mfma_probe_counts_and_runs(dev):
+    """The matrix-unit reference loop reports 2 x its multiply-adds (4 waves x
+    iters x 8 MFMAs of 16 x 16 x 32 per workgroup) and completes with finite
+    results at a rate below the nominal bf16 peak."""
+    wgs, iters = 512, 2000
+    fs.mfma_probe(wgs, iters, dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    flops = fs.mfma_probe(wgs, iters, dev)
+    b.record()
+    torch.cuda.synchronize()
+    assert flops == wgs * 4 * iters * 8 * 2 * 16 * 16 * 32
+    tflops = flops / (a.elapsed_time(b) * 1e-3) / 1e12
+    _say(f"[probe] {tflops:.0f} TFLOP/s")
+    assert 0 < tflops < 2516.6 * 1.02
