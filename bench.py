@@ -112,6 +112,29 @@ def mfma_reference(dev, reps: int = 5):
             "tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
 
 
+def prior_art_timing(w, qd, kd, vd, fwd_ms: float, live_flops: float, reps: int = 10):
+    """The prior-art comparator (fsattn_prior_art_forward: 128-token tiles,
+    window and reference-frame passes, per-element predicates on partly live
+    tiles, merge) on the same inputs, timed with events; the forward's
+    speedup over it is what frame-aligned blocks and the single pass buy."""
+    import torch
+    import frame_block_sparse_amd as fs
+    out = torch.empty_like(qd)
+    ws = torch.empty(max(1, fs.prior_art_workspace_bytes(qd, w)), dtype=torch.uint8, device=qd.device)
+    fs.prior_art_forward(qd, kd, vd, w, out=out, workspace=ws)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        fs.prior_art_forward(qd, kd, vd, w, out=out, workspace=ws)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+    return {"avg_ms": round(ms, 5), "live_tflops": round(live_flops / (ms * 1e-3) / 1e12, 2),
+            "forward_speedup": round(ms / fwd_ms, 3),
+            "what": "128-token tiles over the padded sequence, window pass + reference-frame pass with "
+                    "per-element frame predicates on partly live tiles, online softmax, fp32 (O, lse) merge"}
+
+
 def cpu_baseline(w, q, k, v, budget_s: float):
     """fp64 oracle on a bounded sample of query rows (every frame, every
     head), timed on the host cores. Rate in live TFLOP/s."""
@@ -266,6 +289,7 @@ def main():
     bnd_avg = sum(bnd_ms) / len(bnd_ms)
     achieved = live_flops / (fwd_avg * 1e-3) / 1e12
     ref_mfma = mfma_reference(dev) if w.dtype == "bf16" else None
+    prior = prior_art_timing(w, qd, kd, vd, fwd_avg, live_flops) if w.dtype == "bf16" else None
     value = live_flops / (ms_step * 1e-3) / 1e12
     elig = bnd.host()["eligible"]
     esz = 2 if w.dtype == "bf16" else 4
@@ -304,6 +328,7 @@ def main():
             "frac_of_measured_peak": round(achieved / ref_mfma["tflops"], 4) if ref_mfma else None,
         },
         "partial_tiles_if_128": partial_tile_share(w),
+        "prior_art": prior,
         "plan": {"avg_ms": round(sum(plan_ms) / len(plan_ms), 5), "nnz": nnz},
         "bounds": {"avg_ms": round(bnd_avg, 5), "algorithmic_bytes": bounds_bytes,
                    "GBps": round(bounds_bytes / (bnd_avg * 1e-3) / 1e9, 1), "peak_GBps": PEAK_HBM_GBS},

@@ -151,7 +151,12 @@ __device__ inline bool map_block(const FwdParams &p, int bid, int &f, int &bh, i
 // 48-row waves, 1 above.
 constexpr int fwd_min_waves(int m16) { return m16 <= 2 ? 3 : (m16 == 3 ? 2 : 1); }
 
-template <int M16, int W, int NK16, int NBUF, int D>
+// PRIOR instantiates the prior-art comparator instead of the method: one
+// pass (window or reference frame) over 128-row query tiles of the padded
+// sequence, keys in 128-key tiles with a per-element frame predicate on the
+// tiles that are only partly live, online softmax, normalised fp32 rows and
+// log-sum-exps out (the merge of the two passes is a separate kernel).
+template <int M16, int W, int NK16, int NBUF, int D, bool PRIOR = false>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(fwd_min_waves(M16))))
 void fwd_bf16_kernel(FwdParams p) {
   constexpr int NK = NK16 * 16;
@@ -182,10 +187,17 @@ void fwd_bf16_kernel(FwdParams p) {
   __builtin_assume(wave >= 0 && wave < W);
   const int g = lane >> 4, n16 = lane & 15;
   int f, bh, ti;
-  if (!map_block(p, blockIdx.x, f, bh, ti)) return;
+  if constexpr (PRIOR) {
+    static_assert(!PRIOR || (NK16 == 2 && W * 16 * M16 == 128), "comparator: 128-row tiles, 32-key steps");
+    f = 0;
+    ti = blockIdx.x % p.tiles128;
+    bh = blockIdx.x / p.tiles128;
+  } else {
+    if (!map_block(p, blockIdx.x, f, bh, ti)) return;
+  }
   const int b = bh / p.H, h = bh % p.H;
-  const int row0 = f * p.T + ti * p.rows_per_wg;
-  const int fend = (f + 1) * p.T;   // the frame's end row
+  const int row0 = PRIOR ? ti * 128 : f * p.T + ti * p.rows_per_wg;
+  const int fend = PRIOR ? p.N : (f + 1) * p.T;   // the frame's end row (comparator: the sequence's)
   // A wave whose 16 * M16 rows run past the frame's end (when they do not
   // divide the frame span) computes its rows past the end on the frame's
   // last query row and does not store them.
@@ -214,7 +226,7 @@ void fwd_bf16_kernel(FwdParams p) {
       qf[m][kd] = *reinterpret_cast<const bf16x8 *>(qb + (int64_t)min(qrow0 + 16 * m + n16, fend - 1) * p.qsn +
                                                      32 * kd + 8 * g);
   const int mode = p.flags & 3;
-  const bool may_fix = mode != FSATTN_MODE_FORCE_ONLINE;   // key_mean and rec are given
+  const bool may_fix = !PRIOR && mode != FSATTN_MODE_FORCE_ONLINE;   // key_mean and rec are given
   int eligible = 0;
   float bound = 0.f, kmax = 0.f;
   float4 muv[KD][2];
@@ -229,7 +241,7 @@ void fwd_bf16_kernel(FwdParams p) {
       muv[kd][1] = mu4[8 * kd + 1];
     }
   }
-  if (wave == 0) build_runs(p.row_ptr, p.col_idx, p.nnz, row0 / p.bq, p.bk, p.N, runs, nruns_sm);
+  if (!PRIOR && wave == 0) build_runs(p.row_ptr, p.col_idx, p.nnz, row0 / p.bq, p.bk, p.N, runs, nruns_sm);
 
   // Row sums: the online path adds the probabilities with v_dot2c (it
   // rescales the sum with one multiply); the fixed path sums them on the
@@ -251,11 +263,32 @@ void fwd_bf16_kernel(FwdParams p) {
   // The frame mask gives every query frame at most two runs of live keys
   // (the window, and the reference frame when it is not adjacent to it);
   // the host rejects masks with more. Their bounds live in scalar registers.
-  const int nr = min(*nruns_sm, 2);
-  const int r0s = nr > 0 ? __builtin_amdgcn_readfirstlane(runs[0].x) : 0;
-  const int r0e = nr > 0 ? __builtin_amdgcn_readfirstlane(runs[0].y) : 0;
-  const int r1s = nr > 1 ? __builtin_amdgcn_readfirstlane(runs[1].x) : 0;
-  const int r1e = nr > 1 ? __builtin_amdgcn_readfirstlane(runs[1].y) : 0;
+  int r0s, r0e, r1s, r1e;
+  // comparator: the frames the tile's rows span, and its one key run
+  [[maybe_unused]] int pfa = 0, pfb = 0;
+  if constexpr (PRIOR) {
+    const int last = min(row0 + 128, p.N) - 1;
+    pfa = row0 / p.T;
+    pfb = last / p.T;
+    int ks, ke;
+    if (p.prior_pass == 0) {
+      ks = max(0, pfa - p.wb) * p.T;
+      ke = (min(p.F - 1, pfb + p.wa) + 1) * p.T;
+    } else {
+      ks = p.ref * p.T;
+      ke = (p.ref + 1) * p.T;
+    }
+    // whole 128-key tiles of the padded sequence
+    r0s = ks & ~127;
+    r0e = min((ke + 127) & ~127, p.tiles128 * 128);
+    r1s = r1e = 0;
+  } else {
+    const int nr = min(*nruns_sm, 2);
+    r0s = nr > 0 ? __builtin_amdgcn_readfirstlane(runs[0].x) : 0;
+    r0e = nr > 0 ? __builtin_amdgcn_readfirstlane(runs[0].y) : 0;
+    r1s = nr > 1 ? __builtin_amdgcn_readfirstlane(runs[1].x) : 0;
+    r1e = nr > 1 ? __builtin_amdgcn_readfirstlane(runs[1].y) : 0;
+  }
   // Steps: first the F0 full NK-key steps of run 0 and the F1 of run 1,
   // then the short remainder of each run that has one (16 * k keys, k < NK
   // / 16): the order of the keys does not change the result, and the loop
@@ -345,6 +378,19 @@ void fwd_bf16_kernel(FwdParams p) {
   };
   // copies of step lj (< nsteps) into ring buffer buf
   auto issue_next = [&](int buf) {
+    if constexpr (PRIOR) {
+      // keys past the sequence's end are padding: those steps copy clamped
+      // rows (never read past row N - 1) and the predicate masks them
+      const int row = r0s + NK * lj;
+      if (row + NK <= p.N) {
+        issue_loads(buf, kb + (uint64_t)row * kstep, vb + (uint64_t)row * vstep, true, NK);
+      } else {
+        const int crow = min(row, p.N - 1);
+        issue_loads(buf, kb + (uint64_t)crow * kstep, vb + (uint64_t)crow * vstep, false, p.N - crow);
+      }
+      ++lj;
+      return;
+    }
     if (lj < nfull) {
       if (lj == F0) {
         lkr = k1;
@@ -367,7 +413,7 @@ void fwd_bf16_kernel(FwdParams p) {
   for (int j = 0; j < NBUF - 1; ++j)
     if (lj < nsteps) issue_next(j);
 
-  const bool fixed = mode == FSATTN_MODE_FORCE_FIXED || (mode == FSATTN_MODE_AUTO && eligible != 0);
+  const bool fixed = !PRIOR && (mode == FSATTN_MODE_FORCE_FIXED || (mode == FSATTN_MODE_AUTO && eligible != 0));
   float sh[M16];   // fixed: the row's shift; online: the running max (log2 units)
   if (fixed) {
     const bool per_row = (p.flags & FSATTN_SHIFT_PER_ROW) != 0;
@@ -419,10 +465,27 @@ void fwd_bf16_kernel(FwdParams p) {
   auto kread = [&](unsigned tile, int kd, int t) { return lds_read16(kofs[kd] + tile + 16 * t * ROWB); };
   auto vread = [&](unsigned tile, int dt, int t) { return lds_read_tr(vofs[dt] + tile + 16 * t * ROWB); };
 
+  // Comparator: each row's frame (rows past the end take the last row's),
+  // and whether the 128-key tile holding step key0 is live for every row of
+  // the query tile (then no predicate is needed).
+  [[maybe_unused]] int rowf[M16];
+  if constexpr (PRIOR) {
+#pragma unroll
+    for (int m = 0; m < M16; ++m) rowf[m] = min(wrow0 + 16 * m + n16, p.N - 1) / p.T;
+  }
+  [[maybe_unused]] auto prior_full = [&](int key0) {
+    const int kt0 = key0 & ~127;
+    if (row0 + 128 > p.N || kt0 + 128 > p.N) return false;
+    const int kfa = kt0 / p.T, kfb = (kt0 + 127) / p.T;
+    if (p.prior_pass == 0) return kfa >= pfb - p.wb && kfb <= pfa + p.wa;
+    return kfa == p.ref && kfb == p.ref && (p.ref < pfa - p.wb || p.ref > pfb + p.wa);
+  };
+
   // One chunk of NS 16-key tiles (NS = 2, or 1 for a 16-key tail) whose K
   // rows start at LDS byte offset kt (a multiple of 16 rows into a K tile;
   // the V rows sit TILEB further).
-  auto chunk = [&](auto fixed_tag, auto ns_tag, unsigned kt) {
+  auto chunk = [&](auto fixed_tag, auto ns_tag, unsigned kt, [[maybe_unused]] int key0,
+                   [[maybe_unused]] bool full) {
     constexpr bool FIXED = decltype(fixed_tag)::value;
     constexpr int NS = decltype(ns_tag)::value;
     const unsigned vt = kt + TILEB;
@@ -463,6 +526,30 @@ void fwd_bf16_kernel(FwdParams p) {
           for (int m = 0; m < M16; ++m) s[m][t] = mfma32(a, qf[m][kd], s[m][t]);
         }
     }
+    if constexpr (PRIOR) {
+      // per-element predicate on a partly live key tile: the key's frame
+      // against the row's window (pass 0), or the reference frame for rows
+      // whose window does not hold it (pass 1); padding keys are dead
+      if (!full) {
+        const int kf0 = key0 / p.T, kb1 = (kf0 + 1) * p.T;
+#pragma unroll
+        for (int m = 0; m < M16; ++m)
+#pragma unroll
+          for (int t = 0; t < NS; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = key0 + 16 * t + 4 * g + i;
+              const int kf = kf0 + (key >= kb1 ? 1 : 0);
+              const bool live = key < p.N && (p.prior_pass == 0
+                                                  ? kf >= rowf[m] - p.wb && kf <= rowf[m] + p.wa
+                                                  : kf == p.ref && (p.ref < rowf[m] - p.wb || p.ref > rowf[m] + p.wa));
+              // a read-modify-write (not a masked move): the score register
+              // was just written by an MFMA, and only an instruction that
+              // reads it is held back until that write has landed
+              s[m][t][i] = fminf(s[m][t][i], live ? INFINITY : -INFINITY);
+            }
+      }
+    }
     if constexpr (!FIXED) {
       // Online softmax: raise the running max where a row's chunk maximum
       // exceeds it; rescale only when some row of the wave changed.
@@ -483,7 +570,9 @@ void fwd_bf16_kernel(FwdParams p) {
       if (__any(raised)) {
 #pragma unroll
         for (int m = 0; m < M16; ++m) {
-          const float alpha = __builtin_amdgcn_exp2f(sh[m] - mn[m]);
+          // (a comparator row still without a live key has -inf on both
+          // sides: factor 1, not exp2(NaN))
+          const float alpha = (PRIOR && sh[m] == mn[m]) ? 1.f : __builtin_amdgcn_exp2f(sh[m] - mn[m]);
           sh[m] = mn[m];
           lsum[m] *= alpha;
 #pragma unroll
@@ -508,7 +597,8 @@ void fwd_bf16_kernel(FwdParams p) {
     bf16x4 pt[M16];
 #pragma unroll
     for (int m = 0; m < M16; ++m) {
-      const float nsh = -sh[m];
+      // (a comparator row that has seen no live key yet keeps a max of -inf)
+      const float nsh = (PRIOR && sh[m] == -INFINITY) ? 0.f : -sh[m];
 #pragma unroll
       for (int t = 0; t < NS; ++t)
 #pragma unroll
@@ -589,8 +679,15 @@ void fwd_bf16_kernel(FwdParams p) {
       step_in(i, buf);
       if constexpr (COMPUTE) {
 #pragma unroll
-        for (int c = 0; c < NK / 32; ++c)
-          chunk(fixed_tag, std::integral_constant<int, 2>{}, 2 * buf * TILEB + 32 * c * ROWB);
+        for (int c = 0; c < NK / 32; ++c) {
+          if constexpr (PRIOR) {
+            const int key0 = r0s + NK * i + 32 * c;
+            chunk(fixed_tag, std::integral_constant<int, 2>{}, 2 * buf * TILEB + 32 * c * ROWB, key0,
+                  prior_full(key0));
+          } else {
+            chunk(fixed_tag, std::integral_constant<int, 2>{}, 2 * buf * TILEB + 32 * c * ROWB, 0, true);
+          }
+        }
       }
     };
     int i = 0;
@@ -612,8 +709,8 @@ void fwd_bf16_kernel(FwdParams p) {
         const unsigned k0 = 2 * buf * TILEB + (unsigned)(e0 ? toff0 : toff1) * ROWB;
 #pragma unroll
         for (int c = 0; c < NK / 32 - 1; ++c)
-          if (c < (kl >> 5)) chunk(fixed_tag, std::integral_constant<int, 2>{}, k0 + 32 * c * ROWB);
-        if (kl & 16) chunk(fixed_tag, std::integral_constant<int, 1>{}, k0 + (kl & ~31) * ROWB);
+          if (c < (kl >> 5)) chunk(fixed_tag, std::integral_constant<int, 2>{}, k0 + 32 * c * ROWB, 0, true);
+        if (kl & 16) chunk(fixed_tag, std::integral_constant<int, 1>{}, k0 + (kl & ~31) * ROWB, 0, true);
       }
     }
   };
@@ -638,9 +735,23 @@ void fwd_bf16_kernel(FwdParams p) {
       l += __shfl_xor(l, 16);
       l += __shfl_xor(l, 32);
     }
-    const float inv = 1.f / l;
     const int row = wrow0 + 16 * m + n16;
     if (row >= fend) continue;
+    if constexpr (PRIOR) {
+      // the pass's normalised rows and log-sum-exps (a row with no live key
+      // in this pass: zeros and -inf)
+      const int64_t rr = (int64_t)bh * p.N + row;
+      float *orow = p.part_o + rr * D;
+      const float inv0 = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const f4 x = oacc[m][dt] * inv0;
+        *reinterpret_cast<float4 *>(orow + 16 * dt + 4 * g) = make_float4(x[0], x[1], x[2], x[3]);
+      }
+      if (g == 0) p.part_lse[rr] = l > 0.f ? (sh[m] + log2f(l)) * kLn2 : -INFINITY;
+      continue;
+    }
+    const float inv = 1.f / l;
     if (p.o_f32) {
       float *orow = static_cast<float *>(p.o) + b * p.osb + h * p.osh + (int64_t)row * p.osn;
 #pragma unroll
@@ -664,9 +775,9 @@ void fwd_bf16_kernel(FwdParams p) {
 }
 
 
-template <int M16, int W, int NK16, int NBUF, int D>
+template <int M16, int W, int NK16, int NBUF, int D, bool PRIOR = false>
 hipError_t launch_one(const FwdParams &p, const FwdConfig &c, hipStream_t st) {
-  auto kern = fwd_bf16_kernel<M16, W, NK16, NBUF, D>;
+  auto kern = fwd_bf16_kernel<M16, W, NK16, NBUF, D, PRIOR>;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [&] {
@@ -804,6 +915,65 @@ int fwd_bf16_occupancy(const FwdConfig &c, int head_dim) {
   FSATTN_OCC_CASE(4, 2)
   FSATTN_OCC_CASE(2, 2)
   return 0;
+}
+
+hipError_t launch_prior_pass_bf16(const FwdParams &p, int head_dim, hipStream_t st) {
+  FwdConfig c;
+  c.waves = 4;
+  c.m16 = 2;
+  c.nk16 = 2;
+  c.nbuf = 2;
+  c.lds_bytes = fwd_bf16_lds_bytes(2, 2, head_dim);
+  c.grid = (int64_t)p.tiles128 * p.B * p.H;
+  if (head_dim == 128) return launch_one<2, 4, 2, 2, 128, true>(p, c, st);
+  if (head_dim == 64) return launch_one<2, 4, 2, 2, 64, true>(p, c, st);
+  return hipErrorInvalidValue;
+}
+
+namespace {
+
+// O = the two passes' rows weighted by their exp(lse) (the merge of the
+// prior-art comparator). One thread per 4 output elements.
+__global__ __launch_bounds__(256) void prior_merge_kernel(const float *o_w, const float *lse_w, const float *o_r,
+                                                          const float *lse_r, int H, int N, int D4, void *o,
+                                                          int o_f32, int64_t osb, int64_t osh, int64_t osn,
+                                                          int64_t total) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int64_t rr = idx / D4;
+  const int c = (int)(idx % D4);
+  const int bh = (int)(rr / N), n = (int)(rr % N);
+  const int b = bh / H, h = bh % H;
+  const float lw = lse_w[rr], lr = o_r ? lse_r[rr] : -INFINITY;
+  const float mx = fmaxf(lw, lr);
+  const float ww = lw == -INFINITY ? 0.f : expf(lw - mx), wr = lr == -INFINITY ? 0.f : expf(lr - mx);
+  const float inv = 1.f / (ww + wr);
+  const float4 a = reinterpret_cast<const float4 *>(o_w)[idx];
+  float4 r4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (o_r) r4 = reinterpret_cast<const float4 *>(o_r)[idx];
+  const float y[4] = {(a.x * ww + r4.x * wr) * inv, (a.y * ww + r4.y * wr) * inv, (a.z * ww + r4.z * wr) * inv,
+                      (a.w * ww + r4.w * wr) * inv};
+  const int64_t off = b * osb + h * osh + (int64_t)n * osn + 4 * c;
+  if (o_f32) {
+    *reinterpret_cast<float4 *>(static_cast<float *>(o) + off) = make_float4(y[0], y[1], y[2], y[3]);
+  } else {
+    bf16x4 z;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z[i] = (__bf16)y[i];
+    *reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(o) + off) = z;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prior_merge(const float *o_w, const float *lse_w, const float *o_r, const float *lse_r,
+                              int B, int H, int N, int D, void *o, int o_f32, int64_t osb, int64_t osh,
+                              int64_t osn, hipStream_t st) {
+  const int64_t total = (int64_t)B * H * N * (D / 4);
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(prior_merge_kernel, dim3((unsigned)blocks), dim3(256), 0, st, o_w, lse_w, o_r, lse_r, H, N,
+                     D / 4, o, o_f32, osb, osh, osn, total);
+  return hipGetLastError();
 }
 
 }  // namespace fsattn

@@ -202,6 +202,8 @@ extern "C" fsattn_status fsattn_forward(void *hip_stream, const fsattn_shape *s,
   p.key_mean = key_mean; p.rec = rec; p.lse = lse;
   p.B = s->batch; p.H = s->heads; p.N = s->seq_len; p.F = m->num_frames; p.T = m->tokens_per_frame;
   p.bq = m->block_q; p.bk = m->block_k;
+  p.wb = m->window_before; p.wa = m->window_after; p.ref = m->ref_frame;
+  p.prior_pass = 0; p.tiles128 = 0; p.part_o = p.part_lse = nullptr;
   p.scale = scale; p.scale_log2 = scale * kLog2e;
   p.flags = flags;
   p.o_f32 = o_dtype == FSATTN_F32 ? 1 : 0;
@@ -232,5 +234,85 @@ extern "C" fsattn_status fsattn_mfma_probe(void *hip_stream, int32_t workgroups,
   if (workgroups < 1 || workgroups > (1 << 20) || iters < 1 || !sink) return FSATTN_ERR_INVALID_ARGUMENT;
   if (flops) *flops = mfma_probe_flops(workgroups, iters);
   const hipError_t e = launch_mfma_probe(workgroups, iters, sink, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? FSATTN_OK : FSATTN_ERR_HIP;
+}
+
+namespace {
+
+struct PriorLayout {
+  size_t o_w, lse_w, o_r, lse_r, total;
+};
+
+PriorLayout prior_layout(const fsattn_shape *s) {
+  const int64_t rows = (int64_t)s->batch * s->heads * s->seq_len;
+  PriorLayout l;
+  size_t off = 0;
+  l.o_w = off;   off = align256(off + sizeof(float) * rows * s->head_dim);
+  l.lse_w = off; off = align256(off + sizeof(float) * rows);
+  l.o_r = off;   off = align256(off + sizeof(float) * rows * s->head_dim);
+  l.lse_r = off; off = align256(off + sizeof(float) * rows);
+  l.total = off;
+  return l;
+}
+
+}  // namespace
+
+extern "C" size_t fsattn_prior_art_workspace_bytes(const fsattn_shape *s, const fsattn_mask *m) {
+  if (check_shape(s, m) != FSATTN_OK || s->dtype != FSATTN_BF16) return 0;
+  return prior_layout(s).total;
+}
+
+extern "C" fsattn_status fsattn_prior_art_forward(void *hip_stream, const fsattn_shape *s, const fsattn_mask *m,
+                                                  fsattn_tensor q, fsattn_tensor k, fsattn_tensor v,
+                                                  fsattn_tensor o, int32_t o_dtype, float scale, void *workspace,
+                                                  size_t workspace_bytes) {
+  fsattn_status st = check_shape(s, m);
+  if (st != FSATTN_OK) return st;
+  if (s->dtype != FSATTN_BF16) return FSATTN_ERR_UNSUPPORTED;
+  const int esz = elem_size(s->dtype);
+  if ((st = check_tensor(q, esz, s->head_dim)) != FSATTN_OK) return st;
+  if ((st = check_tensor(k, esz, s->head_dim)) != FSATTN_OK) return st;
+  if ((st = check_tensor(v, esz, s->head_dim)) != FSATTN_OK) return st;
+  if (o_dtype != s->dtype && o_dtype != FSATTN_F32) return FSATTN_ERR_UNSUPPORTED;
+  if ((st = check_tensor(o, elem_size(o_dtype), s->head_dim)) != FSATTN_OK) return st;
+  if (k.stride_n * esz * 64 >= ((int64_t)1 << 31) || v.stride_n * esz * 64 >= ((int64_t)1 << 31))
+    return FSATTN_ERR_UNSUPPORTED;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return FSATTN_ERR_INVALID_ARGUMENT;
+  if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 16) return FSATTN_ERR_INVALID_ARGUMENT;
+  const PriorLayout l = prior_layout(s);
+  if (workspace_bytes < l.total) return FSATTN_ERR_BUFFER_TOO_SMALL;
+  const int64_t tiles = ((int64_t)s->seq_len + 127) / 128;
+  if (tiles * s->batch * s->heads > INT32_MAX) return FSATTN_ERR_UNSUPPORTED;
+
+  FwdParams p = {};
+  p.q = q.data; p.k = k.data; p.v = v.data; p.o = o.data;
+  p.qsb = q.stride_b; p.qsh = q.stride_h; p.qsn = q.stride_n;
+  p.ksb = k.stride_b; p.ksh = k.stride_h; p.ksn = k.stride_n;
+  p.vsb = v.stride_b; p.vsh = v.stride_h; p.vsn = v.stride_n;
+  p.osb = o.stride_b; p.osh = o.stride_h; p.osn = o.stride_n;
+  p.B = s->batch; p.H = s->heads; p.N = s->seq_len; p.F = m->num_frames; p.T = m->tokens_per_frame;
+  p.bq = m->block_q; p.bk = m->block_k;
+  p.wb = m->window_before; p.wa = m->window_after; p.ref = m->ref_frame;
+  p.scale = scale; p.scale_log2 = scale * kLog2e;
+  p.flags = FSATTN_MODE_FORCE_ONLINE;
+  p.o_f32 = o_dtype == FSATTN_F32 ? 1 : 0;
+  p.rows_per_wg = 128;
+  p.tiles128 = (int)tiles;
+  char *base = static_cast<char *>(workspace);
+  float *o_w = reinterpret_cast<float *>(base + l.o_w), *lse_w = reinterpret_cast<float *>(base + l.lse_w);
+  float *o_r = reinterpret_cast<float *>(base + l.o_r), *lse_r = reinterpret_cast<float *>(base + l.lse_r);
+  const hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+  // pass 0: the window; pass 1: the reference frame, for rows whose window
+  // does not hold it; then the merge
+  p.prior_pass = 0; p.part_o = o_w; p.part_lse = lse_w;
+  hipError_t e = launch_prior_pass_bf16(p, s->head_dim, stream);
+  const bool has_ref = m->ref_frame >= 0;
+  if (e == hipSuccess && has_ref) {
+    p.prior_pass = 1; p.part_o = o_r; p.part_lse = lse_r;
+    e = launch_prior_pass_bf16(p, s->head_dim, stream);
+  }
+  if (e == hipSuccess)
+    e = launch_prior_merge(o_w, lse_w, has_ref ? o_r : nullptr, lse_r, p.B, p.H, p.N, s->head_dim, o.data,
+                           p.o_f32, o.stride_b, o.stride_h, o.stride_n, stream);
   return e == hipSuccess ? FSATTN_OK : FSATTN_ERR_HIP;
 }

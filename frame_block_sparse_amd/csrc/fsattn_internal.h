@@ -58,6 +58,12 @@ struct FwdParams {
   uint8_t frame_order[64];
   // Tiles per chunk dealt to one XCD (see dealt_tile).
   int deal_chunk;
+  // Prior-art comparator (tiled passes, see fsattn_prior_art_forward): the
+  // pass (0 window, 1 reference frame), query tiles of 128 rows, and the
+  // pass's normalised fp32 rows [B*H][N][d] and log-sum-exps [B*H][N].
+  int prior_pass, tiles128;
+  int wb, wa, ref;   // the mask's window and reference frame
+  float *part_o, *part_lse;
 };
 constexpr int kMaxOrderedFrames = 64;
 
@@ -102,6 +108,12 @@ bool frame_issue_order(const fsattn_mask *m, uint8_t *order);
 // 2^(override-1) tiles, 15 whole (frame, head) groups. Host only.
 int choose_deal_chunk(const fsattn_shape *s, const fsattn_mask *m, const FwdConfig &c, int override);
 hipError_t launch_forward_f32(const FwdParams &p, int head_dim, hipStream_t st);
+// Prior-art comparator: one tiled pass of the bf16 forward kernel, and the
+// merge of the two passes' rows into O (forward_bf16.hip).
+hipError_t launch_prior_pass_bf16(const FwdParams &p, int head_dim, hipStream_t st);
+hipError_t launch_prior_merge(const float *o_w, const float *lse_w, const float *o_r, const float *lse_r,
+                              int B, int H, int N, int D, void *o, int o_f32, int64_t osb, int64_t osh,
+                              int64_t osn, hipStream_t st);
 // Pure-MFMA reference loop (mfma_probe.hip) and the FLOPs one launch does.
 hipError_t launch_mfma_probe(int workgroups, int iters, float *sink, hipStream_t st);
 int64_t mfma_probe_flops(int workgroups, int iters);

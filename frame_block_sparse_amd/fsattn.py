@@ -84,12 +84,17 @@ def lib() -> ctypes.CDLL:
                                  ctypes.c_void_p, ctypes.c_float, ctypes.c_uint32, ctypes.c_void_p]
     L.fsattn_forward_launch_info.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Mask), ctypes.c_uint32,
                                              c_i32p, c_i32p, c_i32p, c_i64p, c_i32p]
+    L.fsattn_prior_art_forward.argtypes = [ctypes.c_void_p, ctypes.POINTER(Shape), ctypes.POINTER(Mask),
+                                           Tensor, Tensor, Tensor, Tensor, ctypes.c_int32, ctypes.c_float,
+                                           ctypes.c_void_p, ctypes.c_size_t]
+    L.fsattn_prior_art_workspace_bytes.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(Mask)]
+    L.fsattn_prior_art_workspace_bytes.restype = ctypes.c_size_t
     L.fsattn_mfma_probe.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, c_i64p]
     L.fsattn_status_string.argtypes = [ctypes.c_int]
     L.fsattn_status_string.restype = ctypes.c_char_p
     L.fsattn_abi_version.argtypes = []
     for name in ("fsattn_plan_size", "fsattn_plan", "fsattn_plan_device", "fsattn_head_bounds", "fsattn_forward",
-                 "fsattn_forward_launch_info", "fsattn_mfma_probe"):
+                 "fsattn_forward_launch_info", "fsattn_mfma_probe", "fsattn_prior_art_forward"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
@@ -316,3 +321,30 @@ def mfma_probe(workgroups: int, iters: int, device=None, stream: Optional[int] =
                                    int(workgroups), int(iters), sink.data_ptr(), ctypes.byref(flops)),
            "fsattn_mfma_probe")
     return flops.value
+
+
+def prior_art_workspace_bytes(q: torch.Tensor, mask) -> int:
+    """Workspace bytes of fsattn_prior_art_forward for q's shape."""
+    return int(lib().fsattn_prior_art_workspace_bytes(ctypes.byref(_shape(q)), ctypes.byref(to_mask(mask))))
+
+
+def prior_art_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask, scale: Optional[float] = None,
+                      out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                      workspace: Optional[torch.Tensor] = None, stream: Optional[int] = None) -> torch.Tensor:
+    """The comparator (fsattn_prior_art_forward): the same attention with
+    128-token tiles, window and reference-frame passes and a merge."""
+    m = to_mask(mask)
+    s = _shape(q)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype or q.dtype, device=q.device)
+    need = prior_art_workspace_bytes(q, m)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(1, need), dtype=torch.uint8, device=q.device)
+    _check(lib().fsattn_prior_art_forward(stream if stream is not None else _stream(q), ctypes.byref(s),
+                                          ctypes.byref(m), _tensor(q), _tensor(k), _tensor(v), _tensor(out),
+                                          _dtype_code(out), float(scale), workspace.data_ptr(), workspace.numel()),
+           "fsattn_prior_art_forward")
+    return out

@@ -237,6 +237,31 @@ fsattn_status fsattn_forward_launch_info(const fsattn_shape *s, const fsattn_mas
                                          int64_t *workgroups, int32_t *lds_bytes);
 
 /*
+ * Comparator (not part of the attention path): the same attention computed
+ * the way "Deleting the Mask" describes the prior art, so that the gain of
+ * frame-aligned blocks and the single pass can be measured on this device.
+ * The sequence is tiled in 128-token query and key tiles (padded at its
+ * end), not aligned to frames; a first pass covers each row's window, a
+ * second pass the reference frame for the rows whose window does not hold
+ * it; key tiles that are only partly live for a query tile evaluate a
+ * per-element frame predicate; both passes use the online softmax and write
+ * normalised fp32 rows and log-sum-exps to the workspace, and a third kernel
+ * merges them into o. bf16 inputs only (same MFMA, LDS staging and copies as
+ * fsattn_forward's default launch); block_q/block_k of the mask are not
+ * used. workspace: DEVICE memory, 16-byte aligned, >=
+ * fsattn_prior_art_workspace_bytes(). Asynchronous on hip_stream.
+ * Errors: INVALID_ARGUMENT, BLOCK_GEOMETRY, UNSUPPORTED, BUFFER_TOO_SMALL,
+ * HIP.
+ */
+fsattn_status fsattn_prior_art_forward(void *hip_stream, const fsattn_shape *s, const fsattn_mask *m,
+                                       fsattn_tensor q, fsattn_tensor k, fsattn_tensor v, fsattn_tensor o,
+                                       int32_t o_dtype, float scale, void *workspace, size_t workspace_bytes);
+
+/* Workspace bytes of fsattn_prior_art_forward (0 for invalid arguments or
+ * non-bf16 inputs). */
+size_t fsattn_prior_art_workspace_bytes(const fsattn_shape *s, const fsattn_mask *m);
+
+/*
  * Measurement aid (not part of the attention path): a reference rate for
  * the matrix unit. Launches `workgroups` workgroups of 4 waves that each
  * run `iters` rounds of 8 independent v_mfma_f32_16x16x32_bf16 (the forward

@@ -208,3 +208,22 @@ def test_mfma_probe_validates_on_host():
     assert L.fsattn_mfma_probe(None, 1 << 21, 10, FAKE, ctypes.byref(flops)) == 1
     assert L.fsattn_mfma_probe(None, 4, 0, FAKE, ctypes.byref(flops)) == 1
     assert L.fsattn_mfma_probe(None, 4, 10, None, ctypes.byref(flops)) == 1
+
+
+def test_prior_art_forward_validates_on_host():
+    L = fs.lib()
+    s = F.Shape(1, 2, 240, 64, 1)
+    m = F.to_mask((5, 48, 1, 1, 0, 16, 16))
+    need = L.fsattn_prior_art_workspace_bytes(ctypes.byref(s), ctypes.byref(m))
+    assert need >= 2 * 2 * 240 * (64 + 1) * 4
+
+    def call(shape=s, ws=FAKE, wsb=need, scale=0.125, odt=1):
+        return L.fsattn_prior_art_forward(None, ctypes.byref(shape), ctypes.byref(m), _t(), _t(), _t(), _t(), odt,
+                                          scale, ws, wsb)
+    assert call(shape=F.Shape(1, 2, 240, 64, 0)) == 3      # fp32 inputs
+    assert call(ws=None) == 1
+    assert call(ws=FAKE + 8) == 1                          # misaligned workspace
+    assert call(wsb=need - 1) == 4
+    assert call(scale=0.0) == 1
+    assert call(shape=F.Shape(1, 2, 241, 64, 1)) == 1      # seq_len != F*T
+    assert L.fsattn_prior_art_workspace_bytes(ctypes.byref(F.Shape(1, 2, 240, 64, 0)), ctypes.byref(m)) == 0

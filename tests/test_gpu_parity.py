@@ -366,3 +366,49 @@ def test_mfma_probe_counts_and_runs(dev):
     tflops = flops / (a.elapsed_time(b) * 1e-3) / 1e12
     _say(f"[probe] {tflops:.0f} TFLOP/s")
     assert 0 < tflops < 2516.6 * 1.02
+
+
+PRIOR_CASES = [
+    # (name, B, H, F, T, d, dtype, wb, wa, ref, bq, bk): frames that do not divide 128, a padded
+    # sequence end, reference frame outside / inside the window or absent, 16-token frames
+    ("pa_240", 1, 2, 5, 240, 128, "bf16", 1, 1, 0, 48, 48),
+    ("pa_noref_d64", 2, 1, 4, 96, 64, "bf16", 1, 0, -1, 16, 16),
+    ("pa_ref_last", 1, 2, 7, 80, 128, "bf16", 1, 1, 6, 16, 16),
+    ("pa_dense", 1, 1, 3, 256, 128, "bf16", 3, 3, 0, 64, 64),
+    ("pa_t16", 1, 2, 9, 16, 128, "bf16", 2, 0, 4, 16, 16),
+]
+
+
+@pytest.mark.parametrize("case", PRIOR_CASES, ids=[c[0] for c in PRIOR_CASES])
+def test_prior_art_comparator_parity(dev, case):
+    """The prior-art comparator (128-token tiles, window and reference passes,
+    merge) computes the same attention: every element against the oracle, in
+    bf16 and fp32 output."""
+    w, q, k, v = _small(case, seed=8, key_offset=0.5)
+    ref, _ = oracle.attention_ref(q, k, v, _geom(w))
+    qd, kd, vd = (_to_dev(x, torch.bfloat16, dev) for x in (q, k, v))
+    for odt, tol in ((torch.bfloat16, TOL["bf16"]), (torch.float32, 5e-3)):
+        _say(f"[prior-art] {w.name} out={odt}")
+        out = fs.prior_art_forward(qd, kd, vd, w, out_dtype=odt)
+        torch.cuda.synchronize()
+        err = np.abs(out.float().cpu().numpy() - ref).max()
+        assert err <= tol, (odt, err)
+
+
+@pytest.mark.parametrize("i", [2, 5])
+def test_prior_art_comparator_on_workloads(dev, config_inputs, i):
+    """Full-size workloads: sampled rows against the oracle, and every row
+    against fsattn_forward within bf16 rounding."""
+    w = workloads.config(i)
+    q, k, v = config_inputs(i)
+    qd, kd, vd = (_to_dev(x, torch.bfloat16, dev) for x in (q, k, v))
+    _say(f"[prior-art] workload {i}")
+    out = fs.prior_art_forward(qd, kd, vd, w)
+    dp = fs.device_plan(w, dev)
+    bnd = fs.head_bounds(qd, kd, w)
+    mine = fs.forward(qd, kd, vd, dp, bnd)
+    torch.cuda.synchronize()
+    rows = _sample_rows(w, per_frame=16, seed=i)
+    ref, _ = oracle.attention_ref(q, k, v, _geom(w), rows=rows)
+    assert np.abs(out.float().cpu().numpy()[:, :, rows] - ref).max() <= TOL["bf16"]
+    assert (out.float() - mine.float()).abs().max().item() <= TOL["bf16"]
