@@ -86,6 +86,29 @@ __device__ inline bf16x4 lds_read_tr(unsigned addr) {
 // 16-byte LDS read at an LDS byte address.
 __device__ inline bf16x8 lds_read16(unsigned addr) { return *(const lds_bf16x8 *)(uintptr_t)addr; }
 
+// Reductions over the four lanes n, n+16, n+32, n+48 that hold one row's
+// statistics: v_permlane16_swap / v_permlane32_swap leave every lane with
+// its own value and the one of lane l ^ 16 (l ^ 32), in either order, so
+// the max or sum of the two is the pair's (VALU ops, no LDS round trip).
+__device__ inline float pair_max16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_max32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float pair_sum32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float row_max4(float v) { return pair_max32(pair_max16(v)); }
+__device__ inline float row_sum4(float v) { return pair_sum32(pair_sum16(v)); }
+
 // acc + x.lo + x.hi for a packed bf16 pair (v_dot2c_f32_bf16 with (1, 1)).
 __device__ inline float add_bf16_pair(float acc, unsigned x) {
   const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
@@ -430,10 +453,8 @@ void fwd_bf16_kernel(FwdParams p) {
           dot = fmaf(x, mu, dot);
           nq = fmaf(x, x, nq);
         }
-      dot += __shfl_xor(dot, 16);
-      dot += __shfl_xor(dot, 32);
-      nq += __shfl_xor(nq, 16);
-      nq += __shfl_xor(nq, 32);
+      dot = row_sum4(dot);
+      nq = row_sum4(nq);
       const float mrow = per_row ? p.scale * (sqrtf(nq) * kmax + dot) : bound + p.scale * dot;
       sh[m] = mrow * kLog2e;
     }
@@ -562,8 +583,7 @@ void fwd_bf16_kernel(FwdParams p) {
         for (int t = 0; t < NS; ++t)
 #pragma unroll
           for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[m][t][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = row_max4(mx);
         mn[m] = fmaxf(sh[m], mx * c2);
         raised |= mn[m] > sh[m];
       }
@@ -732,8 +752,7 @@ void fwd_bf16_kernel(FwdParams p) {
       l = lsum4[m][0];
     } else {
       l = lsum[m];
-      l += __shfl_xor(l, 16);
-      l += __shfl_xor(l, 32);
+      l = row_sum4(l);
     }
     const int row = wrow0 + 16 * m + n16;
     if (row >= fend) continue;
