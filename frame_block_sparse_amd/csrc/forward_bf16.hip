@@ -174,6 +174,10 @@ __device__ inline bool map_block(const FwdParams &p, int bid, int &f, int &bh, i
 // 48-row waves, 1 above.
 constexpr int fwd_min_waves(int m16) { return m16 <= 2 ? 3 : (m16 == 3 ? 2 : 1); }
 
+// Online path: how far (log2 units) a row's maximum may pass its running
+// shift before the wave rescales.
+constexpr float kLazyRescaleLog2 = 8.f;
+
 // PRIOR instantiates the prior-art comparator instead of the method: one
 // pass (window or reference frame) over 128-row query tiles of the padded
 // sequence, keys in 128-key tiles with a per-element frame predicate on the
@@ -572,8 +576,10 @@ void fwd_bf16_kernel(FwdParams p) {
       }
     }
     if constexpr (!FIXED) {
-      // Online softmax: raise the running max where a row's chunk maximum
-      // exceeds it; rescale only when some row of the wave changed.
+      // Online softmax: raise the running shift to the rows' maxima when
+      // some row of the wave exceeds its shift by more than 2^8 (any shift
+      // at or above a row's maximum gives the same softmax, and weights up
+      // to 2^8 are exact enough in fp32 sums and bf16 P), then rescale.
       float mn[M16];
       bool raised = false;
 #pragma unroll
@@ -585,7 +591,9 @@ void fwd_bf16_kernel(FwdParams p) {
           for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[m][t][i]);
         mx = row_max4(mx);
         mn[m] = fmaxf(sh[m], mx * c2);
-        raised |= mn[m] > sh[m];
+        // lazy: the running shift only has to keep exp2(s - shift) <= 2^8,
+        // so the wave rescales when some row's max passes its shift by more
+        raised |= mn[m] > sh[m] + kLazyRescaleLog2;
       }
       if (__any(raised)) {
 #pragma unroll
