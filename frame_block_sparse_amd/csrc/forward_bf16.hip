@@ -887,7 +887,10 @@ bool choose_fwd_config(const fsattn_shape *s, const fsattn_mask *m, uint32_t fla
     cfg->m16 = m16;
     cfg->nk16 = nk16;
     cfg->nbuf = nbuf;
-    cfg->lds_bytes = fwd_bf16_lds_bytes(nk16, nbuf, s->head_dim);
+    // 48-row waves hold two workgroups per CU by their registers, so a
+    // 4-buffer ring costs them no occupancy (+0.3-0.6 % on 3600-token frames)
+    if (!so && !bo && m16 == 3 && 2 * fwd_bf16_lds_bytes(2, 4, s->head_dim) <= 160 * 1024) cfg->nbuf = 4;
+    cfg->lds_bytes = fwd_bf16_lds_bytes(nk16, cfg->nbuf, s->head_dim);
     cfg->grid = (int64_t)m->num_frames * ((wave_tiles + w - 1) / w) * BH;
     return true;
   }
