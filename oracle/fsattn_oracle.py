@@ -30,7 +30,10 @@ Readings where the pages are silent (each also listed in the design notes):
   R1  softmax scale defaults to 1/sqrt(d)
   R2  the window is inclusive, clamped to [0, F-1], possibly asymmetric
   R3  every query sees the reference frame's keys; reference-frame queries
-      see only their own window (the reference frame is not a global query)
+      see only their own window (the reference frame is not a global query).
+      The symmetric reading, where the reference frame's queries see every
+      frame as a global token's would, is kept as an option
+      (ref_queries_global=1)
   R4  tokens are frame-major: token t belongs to frame t // T
   R5  a plan lists live key blocks in ascending order
   R6  block sizes must be positive multiples of 16 that divide T; anything
@@ -61,12 +64,13 @@ LOG2E = 1.4426950408889634
 # ---------------------------------------------------------------- geometry
 
 class MaskGeometry:
-    """The seven integers that define the frame-structured mask and its
-    block tiling ("Deleting the Mask": window of nearby frames + one
-    reference frame; blocks are multiples of 16 dividing the frame span)."""
+    """The integers that define the frame-structured mask and its block
+    tiling ("Deleting the Mask": window of nearby frames + one reference
+    frame; blocks are multiples of 16 dividing the frame span), plus the
+    R3 option that makes the reference frame's queries global."""
 
     def __init__(self, num_frames, tokens_per_frame, window_before, window_after,
-                 ref_frame, block_q, block_k):
+                 ref_frame, block_q, block_k, ref_queries_global=0):
         self.F = int(num_frames)
         self.T = int(tokens_per_frame)
         self.wb = int(window_before)
@@ -74,6 +78,9 @@ class MaskGeometry:
         self.r = int(ref_frame)
         self.bq = int(block_q)
         self.bk = int(block_k)
+        # R3 option: the reference frame's own queries also see every key
+        self.rg_arg = int(ref_queries_global)
+        self.rg = self.rg_arg if self.r >= 0 else 0
 
     @classmethod
     def from_tuple(cls, t):
@@ -87,7 +94,7 @@ class MaskGeometry:
         """R6: blocks are positive multiples of 16 dividing T; windows are
         non-negative; the reference frame is -1 (none) or a valid frame."""
         ok = (self.F >= 1 and self.T >= 16 and self.wb >= 0 and self.wa >= 0
-              and -1 <= self.r < self.F)
+              and -1 <= self.r < self.F and self.rg_arg in (0, 1))
         for b in (self.bq, self.bk):
             ok = ok and b > 0 and b % 16 == 0 and self.T % b == 0
         if not ok:
@@ -96,7 +103,10 @@ class MaskGeometry:
 
 def live_frames(g: MaskGeometry, f: int) -> List[int]:
     """Frames whose keys the queries of frame f see (R2, R3): the clamped
-    window [f - wb, f + wa] united with the reference frame, ascending."""
+    window [f - wb, f + wa] united with the reference frame, ascending; all
+    frames for the reference frame itself under the R3 option."""
+    if g.rg and f == g.r:
+        return list(range(g.F))
     s = set(range(max(0, f - g.wb), min(g.F - 1, f + g.wa) + 1))
     if g.r >= 0:
         s.add(g.r)
@@ -112,6 +122,8 @@ def token_mask(g: MaskGeometry) -> np.ndarray:
     m = (fj >= fi - g.wb) & (fj <= fi + g.wa)
     if g.r >= 0:
         m |= (fj == g.r)
+    if g.rg:
+        m |= (fi == g.r)
     return m
 
 
@@ -123,6 +135,8 @@ def mask_rows(g: MaskGeometry, rows) -> np.ndarray:
     m = (fr[None, :] >= fi - g.wb) & (fr[None, :] <= fi + g.wa)
     if g.r >= 0:
         m |= (fr[None, :] == g.r)
+    if g.rg:
+        m = m | (fi == g.r)
     return m
 
 
@@ -176,6 +190,8 @@ def partial_blocks_if_tiled(g: MaskGeometry, tile: int) -> Tuple[int, int]:
         m = (fj >= fi - g.wb) & (fj <= fi + g.wa)
         if g.r >= 0:
             m |= (fj == g.r)
+        if g.rg:
+            m = m | (fi == g.r)
         m &= valid[ri][:, None] & valid[None, :]
         blk = m.reshape(tile, nb, tile)
         lv = blk.any(axis=(0, 2))

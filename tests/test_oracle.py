@@ -69,9 +69,10 @@ def test_plan_invariants_random_geometries():
         T = 16 * int(rng.integers(1, 7))
         divs = [b for b in range(16, T + 1, 16) if T % b == 0]
         g = oracle.MaskGeometry(int(rng.integers(1, 8)), T, int(rng.integers(0, 4)), int(rng.integers(0, 4)),
-                                int(rng.integers(-1, 3)), int(rng.choice(divs)), int(rng.choice(divs)))
+                                int(rng.integers(-1, 3)), int(rng.choice(divs)), int(rng.choice(divs)),
+                                int(rng.integers(0, 2)))
         if g.r >= g.F:
-            g.r = -1
+            g.r, g.rg = -1, 0
         rp, ci = oracle.plan_bruteforce(g)
         assert rp[0] == 0 and np.all(np.diff(rp) >= 1)     # every row sees its own frame
         for qb in range(len(rp) - 1):
@@ -97,6 +98,7 @@ def test_invalid_geometry_rejected():
         (3, 48, -1, 1, 0, 16, 16),
         (3, 48, 1, 1, 3, 16, 16),    # reference frame out of range
         (3, 48, 1, 1, -2, 16, 16),
+        (3, 48, 1, 1, 0, 16, 16, 2),  # ref_queries_global is 0 or 1
     ]
     for t in bad:
         with pytest.raises(ValueError):
@@ -115,7 +117,7 @@ def test_partial_block_count_under_coarse_tiles_hand_example():
 
 # ------------------------------------------------------------------ attention
 
-def _bruteforce_attention(q, k, v, F, T, wb, wa, r, scale):
+def _bruteforce_attention(q, k, v, F, T, wb, wa, r, scale, rg=0):
     """Token-by-token softmax with math.exp; the mask is written as frame
     membership tests, independent of the oracle's vectorised rule."""
     B, H, N, d = q.shape
@@ -128,7 +130,7 @@ def _bruteforce_attention(q, k, v, F, T, wb, wa, r, scale):
                 live = []
                 for j in range(N):
                     fj = j // T
-                    if fj in range(fi - wb, fi + wa + 1) or fj == r:
+                    if fj in range(fi - wb, fi + wa + 1) or fj == r or (rg and r >= 0 and fi == r):
                         live.append(j)
                 logits = [scale * sum(q[b, h, i, t] * k[b, h, j, t] for t in range(d)) for j in live]
                 mx = max(logits)
@@ -140,14 +142,16 @@ def _bruteforce_attention(q, k, v, F, T, wb, wa, r, scale):
     return out, lse
 
 
-@pytest.mark.parametrize("geom", [(3, 4, 1, 1, 0), (4, 3, 0, 1, 2), (5, 2, 1, 0, -1), (2, 5, 0, 0, 1)])
+@pytest.mark.parametrize("geom", [(3, 4, 1, 1, 0), (4, 3, 0, 1, 2), (5, 2, 1, 0, -1), (2, 5, 0, 0, 1),
+                                  (4, 3, 0, 0, 2, 1), (5, 2, 1, 0, 0, 1)])
 def test_attention_matches_bruteforce_loops(geom):
-    F, T, wb, wa, r = geom
+    F, T, wb, wa, r = geom[:5]
+    rg = geom[5] if len(geom) > 5 else 0
     rng = np.random.default_rng(F * 100 + T)
     q, k, v = _rand_qkv(rng, 1, 2, F * T, 5)
-    g = oracle.MaskGeometry(F, T, wb, wa, r, 16, 16)     # blocks unused by attention_ref
+    g = oracle.MaskGeometry(F, T, wb, wa, r, 16, 16, rg)     # blocks unused by attention_ref
     o, lse = oracle.attention_ref(q, k, v, g, scale=0.7)
-    ob, lb = _bruteforce_attention(q, k, v, F, T, wb, wa, r, 0.7)
+    ob, lb = _bruteforce_attention(q, k, v, F, T, wb, wa, r, 0.7, rg)
     np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
     np.testing.assert_allclose(lse, lb, rtol=0, atol=1e-12)
 
@@ -289,6 +293,21 @@ def test_bounds_two_frame_window_mean_hand_example():
     assert oracle.head_bounds_ref(q, k, g2, scale=1.0)["c_max"][0, 0] == pytest.approx(0, abs=1e-12)
 
 
+def test_bounds_global_reference_frame_hand_example():
+    # 3 frames x 16 keys in d = 1, window 0, reference frame 0: keys 4, 0, 2 per
+    # frame; mu = 2, every centred key has norm <= 2 (k_max = 2). Keys only:
+    # f0 sees {0} (mean 4), f1 {0,1} (mean 2), f2 {0,2} (mean 3): c_max = 2.
+    # Global reference frame: f0 sees all frames (mean 2 = mu): c_max = 1.
+    k = np.zeros((1, 1, 48, 1)); k[0, 0, :16] = 4.0; k[0, 0, 32:] = 2.0
+    q = np.full((1, 1, 48, 1), 0.5)
+    for rg, c_max in ((0, 2.0), (1, 1.0)):
+        rec = oracle.head_bounds_ref(q, k, oracle.MaskGeometry(3, 16, 0, 0, 0, 16, 16, rg), scale=1.0)
+        assert rec["mu"][0, 0, 0] == pytest.approx(2)
+        assert rec["k_max"][0, 0] == pytest.approx(2)
+        assert rec["c_max"][0, 0] == pytest.approx(c_max)
+        assert rec["gap_est"][0, 0] == pytest.approx(0.5 * (2 + c_max))
+
+
 def test_bounds_degenerate_cases():
     rng = np.random.default_rng(10)
     g = oracle.MaskGeometry(3, 16, 1, 1, 0, 16, 16)
@@ -330,11 +349,12 @@ def _check_bound_audit(q, k, g, rows=None):
 
 def test_bound_audit_exhaustive_small():
     rng = np.random.default_rng(12)
-    for geom in [(5, 16, 1, 1, 0), (6, 16, 2, 0, 3), (4, 32, 0, 0, -1), (7, 16, 1, 1, 0)]:
-        F, T, wb, wa, r = geom
+    for geom in [(5, 16, 1, 1, 0, 0), (6, 16, 2, 0, 3, 0), (4, 32, 0, 0, -1, 0), (7, 16, 1, 1, 0, 0),
+                 (5, 16, 1, 1, 2, 1), (6, 16, 0, 1, 0, 1)]:
+        F, T, wb, wa, r, rg = geom
         q, k, _ = _rand_qkv(rng, 2, 2, F * T, 8)
         k = k + rng.standard_normal(8) * 3
-        _check_bound_audit(q, k, oracle.MaskGeometry(F, T, wb, wa, r, 16, 16))
+        _check_bound_audit(q, k, oracle.MaskGeometry(F, T, wb, wa, r, 16, 16, rg))
 
 
 def test_bound_audit_workload1_exhaustive(config_inputs):
@@ -385,6 +405,10 @@ def test_workload4_stressed_heads_fail_eligibility(config_inputs):
 def test_live_flops_closed_form():
     assert oracle.live_flops(_geom(workloads.config(2).mask_tuple()), 1, 8, 128) == 4 * 128 * 8 * 117 * 960 * 960
     assert oracle.live_flops(_geom(workloads.config(5).mask_tuple()), 1, 4, 128) == 2727346176000
+    # global reference frame 0 of 21 frames with window +-2: frame 0 sees 21
+    # frames instead of 3, so 117 - 3 + 21 = 135 frame pairs
+    g = _geom(workloads.config(2).mask_tuple()[:7] + (1,))
+    assert oracle.live_flops(g, 1, 8, 128) == 4 * 128 * 8 * 135 * 960 * 960
 
 
 # ------------------------------------------------------------------ planted mistakes
@@ -407,6 +431,19 @@ def test_planted_mistake_dropped_reference_frame_is_caught(monkeypatch):
     monkeypatch.setattr(O, "mask_rows", no_ref_rows)
     assert _run_pins_quietly([test_plan_matches_hand_derived_golden,
                               lambda: test_attention_matches_bruteforce_loops((3, 4, 1, 1, 0))]) == 2
+
+
+def test_planted_mistake_ignored_global_reference_queries_is_caught(monkeypatch):
+    def keys_only_rows(g, rows):
+        fr = np.arange(g.N) // g.T
+        fi = (np.asarray(rows) // g.T)[:, None]
+        m = (fr[None, :] >= fi - g.wb) & (fr[None, :] <= fi + g.wa)
+        if g.r >= 0:
+            m |= fr[None, :] == g.r
+        return m
+    monkeypatch.setattr(O, "mask_rows", keys_only_rows)
+    assert _run_pins_quietly([test_plan_matches_hand_derived_golden,
+                              lambda: test_attention_matches_bruteforce_loops((4, 3, 0, 0, 2, 1))]) == 2
 
 
 def test_planted_mistake_exclusive_window_is_caught(monkeypatch):
