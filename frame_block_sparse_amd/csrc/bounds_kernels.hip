@@ -182,11 +182,13 @@ __global__ __launch_bounds__(kHeadThreads) void bounds_head(BoundsParams p) {
 #pragma unroll
   for (int e = 0; e < PER_LANE; ++e) mu[e] = mu_sh[lane + 64 * e];
   // c_max: the largest distance between the mean of the keys a query frame
-  // sees (its window plus the reference frame) and the head's key mean.
+  // sees (its window plus the reference frame; every frame for a global
+  // reference frame's own queries) and the head's key mean.
   // One wave per frame; the squared distance is summed over the wave.
   float cm = 0.f;
   for (int f = wave; f < p.F; f += NW) {
-    const int lo = max(0, f - p.wr), hi = min(p.F - 1, f + p.wa);
+    const bool all = p.ref_global && f == p.ref;
+    const int lo = all ? 0 : max(0, f - p.wr), hi = all ? p.F - 1 : min(p.F - 1, f + p.wa);
     const bool extra = p.ref >= 0 && (p.ref < lo || p.ref > hi);
     const float cnt = (float)(hi - lo + 1 + (extra ? 1 : 0)) * (float)p.T;
     float dd = 0.f;

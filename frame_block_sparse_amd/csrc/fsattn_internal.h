@@ -23,6 +23,7 @@ struct BoundsParams {
   int64_t qsb, qsh, qsn, ksb, ksh, ksn;
   int B, H, N, F, T, D;
   int wr, wa, ref;              // window and reference frame
+  int ref_global;               // the reference frame's queries see every frame
   int chunk, chunks_per_frame;  // token chunk (within one frame)
   float scale, threshold;
   float *key_mean;

@@ -2,8 +2,9 @@
 // Bringing Avatar IV to TPUs", section "Deleting the Mask", Fig. 3).
 //
 // Query frame f sees the key frames of the clamped window
-// [f - window_before, f + window_after] plus the reference frame. With block
-// sizes that are multiples of 16 dividing the frame span, a (query block,
+// [f - window_before, f + window_after] plus the reference frame; with
+// ref_queries_global the reference frame's own queries see every frame.
+// With block sizes that are multiples of 16 dividing the frame span, a (query block,
 // key block) pair is live exactly when the key block's frame is live for
 // the query block's frame, and then every token pair in it is live. So the
 // plan is a frame-level list expanded to blocks: each query block of frame
@@ -24,12 +25,18 @@ bool geometry_ok(const fsattn_mask *m) {
   if (F * T > INT32_MAX) return false;
   if (m->window_before < 0 || m->window_after < 0) return false;
   if (m->ref_frame < -1 || m->ref_frame >= F) return false;
+  if (m->ref_queries_global != 0 && m->ref_queries_global != 1) return false;
   for (int64_t b : {(int64_t)m->block_q, (int64_t)m->block_k})
     if (b <= 0 || b % 16 != 0 || T % b != 0) return false;
   return true;
 }
 
 static void window_of(const fsattn_mask *m, int f, int *lo, int *hi) {
+  if (m->ref_queries_global && m->ref_frame >= 0 && f == m->ref_frame) {
+    *lo = 0;   // a global reference frame's queries see every frame
+    *hi = m->num_frames - 1;
+    return;
+  }
   const int64_t l = std::max<int64_t>(0, (int64_t)f - m->window_before);
   const int64_t h = std::min<int64_t>((int64_t)m->num_frames - 1, (int64_t)f + m->window_after);
   *lo = (int)l;
@@ -108,8 +115,8 @@ extern "C" fsattn_status fsattn_plan(const fsattn_mask *m, int32_t *row_ptr, int
         for (int j = 0; j < n; ++j)
           for (int c = 0; c < kpf; ++c) col_idx[pos++] = frames[j] * kpf + c;
       } else {  // very wide windows: enumerate frames directly, same order
-        int lo = std::max(0, f - m->window_before);
-        int hi = (int)std::min<int64_t>(m->num_frames - 1, (int64_t)f + m->window_after);
+        int lo, hi;
+        window_of(m, f, &lo, &hi);
         const int r = m->ref_frame;
         auto emit = [&](int g) { for (int c = 0; c < kpf; ++c) col_idx[pos++] = g * kpf + c; };
         if (r >= 0 && r < lo) emit(r);

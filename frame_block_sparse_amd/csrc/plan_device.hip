@@ -3,7 +3,8 @@
 // host plan, element for element, straight into device memory.
 //
 // Query frame f sees the key frames of the clamped window
-// [f - window_before, f + window_after] plus the reference frame, so every
+// [f - window_before, f + window_after] plus the reference frame (all frames
+// for a global reference frame's own queries), so every
 // query block of frame f lists the same key blocks: those of its live
 // frames, ascending. One workgroup per query frame finds where the frame's
 // rows start (the sum of the earlier frames' row lengths), then writes its
@@ -19,16 +20,17 @@ namespace {
 constexpr int kPlanThreads = 256;
 
 struct PlanGeom {
-  int F, wb, wa, ref, qpf, kpf;
+  int F, wb, wa, ref, ref_global, qpf, kpf;
 };
 
 // Live frames of query frame f: the clamped window [lo, hi], plus the
 // reference frame before (extra = -1) or after (extra = +1) it, or none
 // (extra = 0) when there is no reference frame or it lies in the window.
 __device__ inline void live_of(const PlanGeom &g, int f, int &lo, int &hi, int &extra) {
+  const bool all = g.ref_global && f == g.ref;
   const int64_t l = (int64_t)f - g.wb, h = (int64_t)f + g.wa;   // (windows may be wider than F)
-  lo = l < 0 ? 0 : (int)l;
-  hi = h > g.F - 1 ? g.F - 1 : (int)h;
+  lo = all || l < 0 ? 0 : (int)l;
+  hi = all || h > g.F - 1 ? g.F - 1 : (int)h;
   extra = 0;
   if (g.ref >= 0 && g.ref < lo) extra = -1;
   if (g.ref >= 0 && g.ref > hi) extra = 1;
@@ -80,6 +82,7 @@ hipError_t launch_plan_device(const fsattn_mask &m, int32_t *row_ptr, int32_t *c
   g.wb = m.window_before;
   g.wa = m.window_after;
   g.ref = m.ref_frame;
+  g.ref_global = m.ref_queries_global;
   g.qpf = m.tokens_per_frame / m.block_q;
   g.kpf = m.tokens_per_frame / m.block_k;
   hipLaunchKernelGGL(plan_kernel, dim3(g.F), dim3(kPlanThreads), 0, st, g, row_ptr, col_idx);

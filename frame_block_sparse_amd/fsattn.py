@@ -19,6 +19,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfsattn.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fsattn.h")
 
+# the layout of the structures below (FSATTN_ABI_VERSION of the header)
+ABI_VERSION = 2
+
 F32, BF16 = 0, 1
 MODE_AUTO, MODE_FORCE_ONLINE, MODE_FORCE_FIXED, SHIFT_PER_ROW = 0, 1, 2, 4
 DEFAULT_GAP_NATS = 30.0
@@ -30,7 +33,8 @@ STATUS_NAMES = {0: "FSATTN_OK", 1: "FSATTN_ERR_INVALID_ARGUMENT", 2: "FSATTN_ERR
 class Mask(ctypes.Structure):
     _fields_ = [("num_frames", ctypes.c_int32), ("tokens_per_frame", ctypes.c_int32),
                 ("window_before", ctypes.c_int32), ("window_after", ctypes.c_int32),
-                ("ref_frame", ctypes.c_int32), ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32)]
+                ("ref_frame", ctypes.c_int32), ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32),
+                ("ref_queries_global", ctypes.c_int32)]
 
 
 class Shape(ctypes.Structure):
@@ -93,6 +97,9 @@ def lib() -> ctypes.CDLL:
     L.fsattn_status_string.argtypes = [ctypes.c_int]
     L.fsattn_status_string.restype = ctypes.c_char_p
     L.fsattn_abi_version.argtypes = []
+    if L.fsattn_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH} has ABI {L.fsattn_abi_version()}, the binding expects {ABI_VERSION}: "
+                           "rebuild it")
     for name in ("fsattn_plan_size", "fsattn_plan", "fsattn_plan_device", "fsattn_head_bounds", "fsattn_forward",
                  "fsattn_forward_launch_info", "fsattn_mfma_probe", "fsattn_prior_art_forward"):
         getattr(L, name).restype = ctypes.c_int
@@ -120,14 +127,17 @@ def _check(st: int, what: str):
 
 
 def to_mask(mask) -> Mask:
-    """A Mask from a Mask, a 7-tuple (num_frames, tokens_per_frame,
-    window_before, window_after, ref_frame, block_q, block_k) or any object
-    with a mask_tuple() method."""
+    """A Mask from a Mask, a 7- or 8-tuple (num_frames, tokens_per_frame,
+    window_before, window_after, ref_frame, block_q, block_k
+    [, ref_queries_global]) or any object with a mask_tuple() method."""
     if isinstance(mask, Mask):
         return mask
     if hasattr(mask, "mask_tuple"):
         mask = mask.mask_tuple()
-    return Mask(*[int(x) for x in mask])
+    vals = [int(x) for x in mask]
+    if len(vals) not in (7, 8):
+        raise ValueError(f"a mask has 7 or 8 integers, got {len(vals)}")
+    return Mask(*vals)
 
 
 def _dtype_code(t: torch.Tensor) -> int:

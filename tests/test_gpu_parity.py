@@ -4,6 +4,7 @@ Tolerances: max-abs <= 1e-5 for fp32 inputs and <= 2e-2 for bf16 inputs
 (fp32 accumulation, P rounded to bf16 for PV, bf16 output). Bound records:
 relative 1e-5 (fp32 reductions vs fp64), eligibility decisions equal.
 """
+import dataclasses
 import math
 import sys
 
@@ -88,13 +89,14 @@ def test_plan_device_bit_exact_on_workloads(dev, i):
 
 def test_plan_device_bit_exact_on_random_geometries(dev):
     rng = np.random.default_rng(11)
-    cases = [(3, 32, 10 ** 6, 10 ** 6, 1, 16, 32), (1, 16, 0, 0, -1, 16, 16), (7, 48, 0, 2, 6, 48, 16)]
+    cases = [(3, 32, 10 ** 6, 10 ** 6, 1, 16, 32), (1, 16, 0, 0, -1, 16, 16), (7, 48, 0, 2, 6, 48, 16),
+             (7, 48, 0, 2, 6, 48, 16, 1), (9, 32, 1, 1, 4, 16, 32, 1)]
     for _ in range(40):
         T = 16 * int(rng.integers(1, 7))
         divs = [b for b in range(16, T + 1, 16) if T % b == 0]
         F_ = int(rng.integers(1, 12))
         cases.append((F_, T, int(rng.integers(0, 4)), int(rng.integers(0, 4)), int(rng.integers(-1, F_)),
-                      int(rng.choice(divs)), int(rng.choice(divs))))
+                      int(rng.choice(divs)), int(rng.choice(divs)), int(rng.integers(0, 2))))
     for g in cases:
         rp, ci = fs.plan(g)
         dp = fs.plan_on_device(g, dev)
@@ -309,6 +311,57 @@ def test_forward_workload_parity(dev, config_inputs, i):
     assert np.isfinite(o).all()
     vmax = np.abs(v).max(axis=2, keepdims=True)
     assert np.all(np.abs(o) <= vmax * (1 + 2 ** -7) + 1e-6)
+
+
+# The reference frame as a global token in both directions: its own queries
+# see every frame (mask option ref_queries_global).
+GLOBAL_REF = [
+    # (name, B, H, F, T, d, dtype, wb, wa, ref, bq, bk)
+    ("gref_mid", 1, 2, 6, 160, 128, "bf16", 1, 1, 2, 32, 32),
+    ("gref0_d64", 2, 2, 5, 96, 64, "bf16", 0, 0, 0, 48, 16),
+    ("gref_last_tail", 1, 3, 4, 240, 128, "bf16", 1, 0, 3, 48, 80),
+    ("gref_f32", 1, 2, 4, 80, 128, "f32", 1, 0, 3, 16, 80),
+]
+
+
+@pytest.mark.parametrize("case", GLOBAL_REF, ids=[c[0] for c in GLOBAL_REF])
+@pytest.mark.parametrize("mode", ["auto", "online", "fixed"])
+def test_forward_global_reference_frame_parity(dev, case, mode):
+    w, q, k, v = _small(case, seed=4, key_offset=1.5)
+    w = dataclasses.replace(w, ref_queries_global=1)
+    _say(f"[fwd-gref] {w.name} mode={mode}")
+    out, bnd, lse = _run(w, q, k, v, dev, flags=fs.make_flags(mode), lse=True)
+    g = _geom(w)
+    rec = oracle.head_bounds_ref(q, k, g)
+    got = bnd.host()
+    np.testing.assert_allclose(got["c_max"], rec["c_max"], rtol=1e-4, atol=1e-5 * float(rec["k_max"].max()))
+    ref, ref_lse = oracle.attention_ref(q, k, v, g)
+    err = np.abs(out.float().cpu().numpy() - ref).max()
+    assert err <= TOL[w.dtype], err
+    lerr = np.abs(lse.cpu().numpy() - ref_lse).max()
+    assert lerr <= LSE_TOL[w.dtype], lerr
+
+
+def test_forward_global_reference_frame_full_size(dev, config_inputs):
+    """21 frames x 960 tokens with a global reference frame 0, in the
+    library's default launch: bounds against the oracle, and sampled rows of
+    every frame (frame 0's rows see all 20,160 keys) against it."""
+    w = dataclasses.replace(workloads.config(2), ref_queries_global=1)
+    _say(f"[fwd-gref] {w.name} + global reference frame")
+    q, k, v = config_inputs(2)
+    out, bnd, _ = _run(w, q, k, v, dev)
+    g = _geom(w)
+    rec = oracle.head_bounds_ref(q, k, g)
+    got = bnd.host()
+    np.testing.assert_allclose(got["c_max"], rec["c_max"], rtol=1e-4, atol=1e-5 * float(rec["k_max"].max()))
+    assert np.array_equal(got["eligible"].astype(bool), rec["eligible"])
+    rows = _sample_rows(w, per_frame=24, seed=9)
+    ref, _ = oracle.attention_ref(q, k, v, g, rows=rows)
+    o = out.float().cpu().numpy()
+    err = np.abs(o[:, :, rows] - ref).max()
+    _say(f"    max abs err {err:.3e}")
+    assert err <= TOL[w.dtype], err
+    assert np.isfinite(o).all()
 
 
 def test_online_and_fixed_agree_on_eligible_heads(dev, config_inputs):
