@@ -33,7 +33,11 @@ Readings where the pages are silent (each also listed in the design notes):
       see only their own window (the reference frame is not a global query).
       The symmetric reading, where the reference frame's queries see every
       frame as a global token's would, is kept as an option
-      (ref_queries_global=1)
+      (ref_queries_global=1).
+  R3b several reference frames: a contiguous span of ref_count frames
+      starting at the reference frame (ref_count 0 or 1: the one frame);
+      every query sees all of their keys, and under the R3 option the
+      queries of every frame of the span are global
   R4  tokens are frame-major: token t belongs to frame t // T
   R5  a plan lists live key blocks in ascending order
   R6  block sizes must be positive multiples of 16 that divide T; anything
@@ -67,10 +71,11 @@ class MaskGeometry:
     """The integers that define the frame-structured mask and its block
     tiling ("Deleting the Mask": window of nearby frames + one reference
     frame; blocks are multiples of 16 dividing the frame span), plus the
-    R3 option that makes the reference frame's queries global."""
+    R3 option that makes the reference frame's queries global and the R3b
+    span of several reference frames."""
 
     def __init__(self, num_frames, tokens_per_frame, window_before, window_after,
-                 ref_frame, block_q, block_k, ref_queries_global=0):
+                 ref_frame, block_q, block_k, ref_queries_global=0, ref_count=0):
         self.F = int(num_frames)
         self.T = int(tokens_per_frame)
         self.wb = int(window_before)
@@ -81,6 +86,9 @@ class MaskGeometry:
         # R3 option: the reference frame's own queries also see every key
         self.rg_arg = int(ref_queries_global)
         self.rg = self.rg_arg if self.r >= 0 else 0
+        # R3b: reference frames r .. r + nr - 1 (nr = 0 without a reference frame)
+        self.nr_arg = int(ref_count)
+        self.nr = max(1, self.nr_arg) if self.r >= 0 else 0
 
     @classmethod
     def from_tuple(cls, t):
@@ -94,7 +102,8 @@ class MaskGeometry:
         """R6: blocks are positive multiples of 16 dividing T; windows are
         non-negative; the reference frame is -1 (none) or a valid frame."""
         ok = (self.F >= 1 and self.T >= 16 and self.wb >= 0 and self.wa >= 0
-              and -1 <= self.r < self.F and self.rg_arg in (0, 1))
+              and -1 <= self.r < self.F and self.rg_arg in (0, 1)
+              and self.nr_arg >= 0 and self.r + self.nr <= self.F)
         for b in (self.bq, self.bk):
             ok = ok and b > 0 and b % 16 == 0 and self.T % b == 0
         if not ok:
@@ -102,14 +111,14 @@ class MaskGeometry:
 
 
 def live_frames(g: MaskGeometry, f: int) -> List[int]:
-    """Frames whose keys the queries of frame f see (R2, R3): the clamped
-    window [f - wb, f + wa] united with the reference frame, ascending; all
-    frames for the reference frame itself under the R3 option."""
-    if g.rg and f == g.r:
+    """Frames whose keys the queries of frame f see (R2, R3, R3b): the
+    clamped window [f - wb, f + wa] united with the reference frames, ascending; all
+    frames for a reference frame itself under the R3 option."""
+    refs = range(g.r, g.r + g.nr)
+    if g.rg and f in refs:
         return list(range(g.F))
     s = set(range(max(0, f - g.wb), min(g.F - 1, f + g.wa) + 1))
-    if g.r >= 0:
-        s.add(g.r)
+    s.update(refs)
     return sorted(s)
 
 
@@ -120,10 +129,9 @@ def token_mask(g: MaskGeometry) -> np.ndarray:
     fi = fr[:, None]
     fj = fr[None, :]
     m = (fj >= fi - g.wb) & (fj <= fi + g.wa)
-    if g.r >= 0:
-        m |= (fj == g.r)
+    m |= (fj >= g.r) & (fj < g.r + g.nr)
     if g.rg:
-        m |= (fi == g.r)
+        m |= (fi >= g.r) & (fi < g.r + g.nr)
     return m
 
 
@@ -133,10 +141,9 @@ def mask_rows(g: MaskGeometry, rows) -> np.ndarray:
     fr = np.arange(g.N) // g.T
     fi = (np.asarray(rows, dtype=np.int64) // g.T)[:, None]
     m = (fr[None, :] >= fi - g.wb) & (fr[None, :] <= fi + g.wa)
-    if g.r >= 0:
-        m |= (fr[None, :] == g.r)
+    m |= (fr[None, :] >= g.r) & (fr[None, :] < g.r + g.nr)
     if g.rg:
-        m = m | (fi == g.r)
+        m = m | ((fi >= g.r) & (fi < g.r + g.nr))
     return m
 
 
@@ -188,10 +195,9 @@ def partial_blocks_if_tiled(g: MaskGeometry, tile: int) -> Tuple[int, int]:
         fi = fr[ri][:, None]
         fj = fr[None, :]
         m = (fj >= fi - g.wb) & (fj <= fi + g.wa)
-        if g.r >= 0:
-            m |= (fj == g.r)
+        m |= (fj >= g.r) & (fj < g.r + g.nr)
         if g.rg:
-            m = m | (fi == g.r)
+            m = m | ((fi >= g.r) & (fi < g.r + g.nr))
         m &= valid[ri][:, None] & valid[None, :]
         blk = m.reshape(tile, nb, tile)
         lv = blk.any(axis=(0, 2))

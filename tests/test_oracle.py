@@ -70,9 +70,9 @@ def test_plan_invariants_random_geometries():
         divs = [b for b in range(16, T + 1, 16) if T % b == 0]
         g = oracle.MaskGeometry(int(rng.integers(1, 8)), T, int(rng.integers(0, 4)), int(rng.integers(0, 4)),
                                 int(rng.integers(-1, 3)), int(rng.choice(divs)), int(rng.choice(divs)),
-                                int(rng.integers(0, 2)))
-        if g.r >= g.F:
-            g.r, g.rg = -1, 0
+                                int(rng.integers(0, 2)), int(rng.integers(0, 3)))
+        if g.r + g.nr > g.F:
+            g = oracle.MaskGeometry(g.F, g.T, g.wb, g.wa, -1, g.bq, g.bk)
         rp, ci = oracle.plan_bruteforce(g)
         assert rp[0] == 0 and np.all(np.diff(rp) >= 1)     # every row sees its own frame
         for qb in range(len(rp) - 1):
@@ -99,6 +99,8 @@ def test_invalid_geometry_rejected():
         (3, 48, 1, 1, 3, 16, 16),    # reference frame out of range
         (3, 48, 1, 1, -2, 16, 16),
         (3, 48, 1, 1, 0, 16, 16, 2),  # ref_queries_global is 0 or 1
+        (3, 48, 1, 1, 2, 16, 16, 0, 2),   # reference span past the last frame
+        (3, 48, 1, 1, 0, 16, 16, 0, -1),
     ]
     for t in bad:
         with pytest.raises(ValueError):
@@ -117,10 +119,11 @@ def test_partial_block_count_under_coarse_tiles_hand_example():
 
 # ------------------------------------------------------------------ attention
 
-def _bruteforce_attention(q, k, v, F, T, wb, wa, r, scale, rg=0):
+def _bruteforce_attention(q, k, v, F, T, wb, wa, r, scale, rg=0, nr=0):
     """Token-by-token softmax with math.exp; the mask is written as frame
     membership tests, independent of the oracle's vectorised rule."""
     B, H, N, d = q.shape
+    refs = list(range(r, r + max(1, nr))) if r >= 0 else []
     out = np.zeros((B, H, N, d))
     lse = np.zeros((B, H, N))
     for b in range(B):
@@ -130,7 +133,7 @@ def _bruteforce_attention(q, k, v, F, T, wb, wa, r, scale, rg=0):
                 live = []
                 for j in range(N):
                     fj = j // T
-                    if fj in range(fi - wb, fi + wa + 1) or fj == r or (rg and r >= 0 and fi == r):
+                    if fj in range(fi - wb, fi + wa + 1) or fj in refs or (rg and fi in refs):
                         live.append(j)
                 logits = [scale * sum(q[b, h, i, t] * k[b, h, j, t] for t in range(d)) for j in live]
                 mx = max(logits)
@@ -143,15 +146,17 @@ def _bruteforce_attention(q, k, v, F, T, wb, wa, r, scale, rg=0):
 
 
 @pytest.mark.parametrize("geom", [(3, 4, 1, 1, 0), (4, 3, 0, 1, 2), (5, 2, 1, 0, -1), (2, 5, 0, 0, 1),
-                                  (4, 3, 0, 0, 2, 1), (5, 2, 1, 0, 0, 1)])
+                                  (4, 3, 0, 0, 2, 1), (5, 2, 1, 0, 0, 1), (6, 2, 0, 0, 1, 0, 3),
+                                  (5, 3, 1, 0, 2, 1, 2)])
 def test_attention_matches_bruteforce_loops(geom):
     F, T, wb, wa, r = geom[:5]
     rg = geom[5] if len(geom) > 5 else 0
+    nr = geom[6] if len(geom) > 6 else 0
     rng = np.random.default_rng(F * 100 + T)
     q, k, v = _rand_qkv(rng, 1, 2, F * T, 5)
-    g = oracle.MaskGeometry(F, T, wb, wa, r, 16, 16, rg)     # blocks unused by attention_ref
+    g = oracle.MaskGeometry(F, T, wb, wa, r, 16, 16, rg, nr)     # blocks unused by attention_ref
     o, lse = oracle.attention_ref(q, k, v, g, scale=0.7)
-    ob, lb = _bruteforce_attention(q, k, v, F, T, wb, wa, r, 0.7, rg)
+    ob, lb = _bruteforce_attention(q, k, v, F, T, wb, wa, r, 0.7, rg, nr)
     np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
     np.testing.assert_allclose(lse, lb, rtol=0, atol=1e-12)
 
@@ -308,6 +313,24 @@ def test_bounds_global_reference_frame_hand_example():
         assert rec["gap_est"][0, 0] == pytest.approx(0.5 * (2 + c_max))
 
 
+def test_bounds_reference_span_hand_example():
+    # 4 frames x 16 keys in d = 1, window 0, reference frames 0-1 (span 2):
+    # keys 6, 2, 0, -4 per frame; mu = 1, k_max = |-4 - 1| = 5. Frames 0 and 1
+    # see {0,1} (mean 4), frame 2 {0,1,2} (mean 8/3), frame 3 {0,1,3} (mean 4/3):
+    # c_max = 3. One reference frame 0 instead: f0 {0} (6), f1 {0,1} (4),
+    # f2 {0,2} (3), f3 {0,3} (1): c_max = 5.
+    k = np.zeros((1, 1, 64, 1))
+    for f, val in enumerate((6.0, 2.0, 0.0, -4.0)):
+        k[0, 0, 16 * f:16 * (f + 1)] = val
+    q = np.full((1, 1, 64, 1), 0.25)
+    for nr, c_max in ((2, 3.0), (1, 5.0), (0, 5.0)):
+        rec = oracle.head_bounds_ref(q, k, oracle.MaskGeometry(4, 16, 0, 0, 0, 16, 16, 0, nr), scale=1.0)
+        assert rec["mu"][0, 0, 0] == pytest.approx(1)
+        assert rec["k_max"][0, 0] == pytest.approx(5)
+        assert rec["c_max"][0, 0] == pytest.approx(c_max)
+        assert rec["gap_est"][0, 0] == pytest.approx(0.25 * (5 + c_max))
+
+
 def test_bounds_degenerate_cases():
     rng = np.random.default_rng(10)
     g = oracle.MaskGeometry(3, 16, 1, 1, 0, 16, 16)
@@ -350,11 +373,12 @@ def _check_bound_audit(q, k, g, rows=None):
 def test_bound_audit_exhaustive_small():
     rng = np.random.default_rng(12)
     for geom in [(5, 16, 1, 1, 0, 0), (6, 16, 2, 0, 3, 0), (4, 32, 0, 0, -1, 0), (7, 16, 1, 1, 0, 0),
-                 (5, 16, 1, 1, 2, 1), (6, 16, 0, 1, 0, 1)]:
-        F, T, wb, wa, r, rg = geom
+                 (5, 16, 1, 1, 2, 1), (6, 16, 0, 1, 0, 1), (7, 16, 0, 0, 2, 0, 3), (6, 16, 1, 0, 4, 1, 2)]:
+        F, T, wb, wa, r, rg = geom[:6]
+        nr = geom[6] if len(geom) > 6 else 0
         q, k, _ = _rand_qkv(rng, 2, 2, F * T, 8)
         k = k + rng.standard_normal(8) * 3
-        _check_bound_audit(q, k, oracle.MaskGeometry(F, T, wb, wa, r, 16, 16, rg))
+        _check_bound_audit(q, k, oracle.MaskGeometry(F, T, wb, wa, r, 16, 16, rg, nr))
 
 
 def test_bound_audit_workload1_exhaustive(config_inputs):
@@ -409,6 +433,12 @@ def test_live_flops_closed_form():
     # frames instead of 3, so 117 - 3 + 21 = 135 frame pairs
     g = _geom(workloads.config(2).mask_tuple()[:7] + (1,))
     assert oracle.live_flops(g, 1, 8, 128) == 4 * 128 * 8 * 135 * 960 * 960
+    # reference frames 0-1 of 21 with window +-2: frames 0..3 see 3, 4, 5, 6
+    # frames, 4..18 see 5 + 2, and 19, 20 (window clamped) 4 + 2 and 3 + 2:
+    # 18 + 15 * 7 + 11 = 134 frame pairs
+    g = _geom(workloads.config(2).mask_tuple()[:7] + (0, 2))
+    assert [len(oracle.live_frames(g, f)) for f in (0, 1, 2, 3, 4, 18, 19, 20)] == [3, 4, 5, 6, 7, 7, 6, 5]
+    assert oracle.live_flops(g, 1, 8, 128) == 4 * 128 * 8 * 134 * 960 * 960
 
 
 # ------------------------------------------------------------------ planted mistakes
@@ -444,6 +474,21 @@ def test_planted_mistake_ignored_global_reference_queries_is_caught(monkeypatch)
     monkeypatch.setattr(O, "mask_rows", keys_only_rows)
     assert _run_pins_quietly([test_plan_matches_hand_derived_golden,
                               lambda: test_attention_matches_bruteforce_loops((4, 3, 0, 0, 2, 1))]) == 2
+
+
+def test_planted_mistake_single_reference_frame_is_caught(monkeypatch):
+    def first_ref_only_rows(g, rows):
+        fr = np.arange(g.N) // g.T
+        fi = (np.asarray(rows) // g.T)[:, None]
+        m = (fr[None, :] >= fi - g.wb) & (fr[None, :] <= fi + g.wa)
+        if g.r >= 0:
+            m |= fr[None, :] == g.r
+            if g.rg:
+                m = m | (fi == g.r)
+        return m
+    monkeypatch.setattr(O, "mask_rows", first_ref_only_rows)
+    assert _run_pins_quietly([test_plan_matches_hand_derived_golden,
+                              lambda: test_attention_matches_bruteforce_loops((6, 2, 0, 0, 1, 0, 3))]) == 2
 
 
 def test_planted_mistake_exclusive_window_is_caught(monkeypatch):
