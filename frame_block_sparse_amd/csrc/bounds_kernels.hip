@@ -182,23 +182,21 @@ __global__ __launch_bounds__(kHeadThreads) void bounds_head(BoundsParams p) {
 #pragma unroll
   for (int e = 0; e < PER_LANE; ++e) mu[e] = mu_sh[lane + 64 * e];
   // c_max: the largest distance between the mean of the keys a query frame
-  // sees (its window plus the reference frame; every frame for a global
-  // reference frame's own queries) and the head's key mean.
+  // sees (its window plus the reference frames; every frame for the queries
+  // of global reference frames) and the head's key mean.
   // One wave per frame; the squared distance is summed over the wave.
   float cm = 0.f;
   for (int f = wave; f < p.F; f += NW) {
-    const bool all = p.ref_global && f == p.ref;
-    const int lo = all ? 0 : max(0, f - p.wr), hi = all ? p.F - 1 : min(p.F - 1, f + p.wa);
-    const bool extra = p.ref >= 0 && (p.ref < lo || p.ref > hi);
-    const float cnt = (float)(hi - lo + 1 + (extra ? 1 : 0)) * (float)p.T;
+    int iv[4];
+    const int nint = live_intervals(p.live, f, iv);
+    const int n0 = iv[1] - iv[0] + 1, n1 = nint == 2 ? iv[3] - iv[2] + 1 : 0;
+    const float cnt = (float)(n0 + n1) * (float)p.T;
     float dd = 0.f;
 #pragma unroll
     for (int e = 0; e < PER_LANE; ++e) {
       const int j = lane + 64 * e;
-      float w = 0.f;
-      if (extra && p.ref < lo) w += S[(int64_t)p.ref * D + j];
-      w += ordered_sum(S + (int64_t)lo * D + j, hi - lo + 1, D);
-      if (extra && p.ref > hi) w += S[(int64_t)p.ref * D + j];
+      float w = ordered_sum(S + (int64_t)iv[0] * D + j, n0, D);
+      if (n1) w += ordered_sum(S + (int64_t)iv[2] * D + j, n1, D);
       const float dlt = w / cnt - mu[e];
       dd = fmaf(dlt, dlt, dd);
     }

@@ -115,8 +115,7 @@ extern "C" fsattn_status fsattn_head_bounds(void *hip_stream, const fsattn_shape
   p.ksb = k.stride_b; p.ksh = k.stride_h; p.ksn = k.stride_n;
   p.B = s->batch; p.H = s->heads; p.N = s->seq_len; p.F = m->num_frames; p.T = m->tokens_per_frame;
   p.D = s->head_dim;
-  p.wr = m->window_before; p.wa = m->window_after; p.ref = m->ref_frame;
-  p.ref_global = m->ref_frame >= 0 ? m->ref_queries_global : 0;
+  p.live = live_geom(*m);
   p.chunk = kBoundsChunk; p.chunks_per_frame = w.chunks_per_frame;
   p.scale = scale; p.threshold = gap_threshold_nats;
   p.key_mean = key_mean; p.rec = rec;
@@ -270,7 +269,7 @@ extern "C" fsattn_status fsattn_prior_art_forward(void *hip_stream, const fsattn
   fsattn_status st = check_shape(s, m);
   if (st != FSATTN_OK) return st;
   if (s->dtype != FSATTN_BF16) return FSATTN_ERR_UNSUPPORTED;
-  if (m->ref_frame >= 0 && m->ref_queries_global) return FSATTN_ERR_UNSUPPORTED;
+  if (m->ref_frame >= 0 && (m->ref_queries_global || m->ref_count > 1)) return FSATTN_ERR_UNSUPPORTED;
   const int esz = elem_size(s->dtype);
   if ((st = check_tensor(q, esz, s->head_dim)) != FSATTN_OK) return st;
   if ((st = check_tensor(k, esz, s->head_dim)) != FSATTN_OK) return st;

@@ -10,6 +10,54 @@ constexpr int kMaxRuns = 64;        // contiguous key runs per query frame kept 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// The mask's frame geometry as the kernels see it: the window, and the
+// reference frames r .. r + nr - 1 (nr = 0 without reference frames), whose
+// own queries see every frame when rg is set.
+struct LiveGeom {
+  int F, wb, wa, r, nr, rg;
+};
+
+inline LiveGeom live_geom(const fsattn_mask &m) {
+  LiveGeom g;
+  g.F = m.num_frames;
+  g.wb = m.window_before;
+  g.wa = m.window_after;
+  g.r = m.ref_frame;
+  g.nr = m.ref_frame >= 0 ? (m.ref_count > 1 ? m.ref_count : 1) : 0;
+  g.rg = m.ref_frame >= 0 ? m.ref_queries_global : 0;
+  return g;
+}
+
+// The frames whose keys the queries of frame f see, as one or two disjoint,
+// non-adjacent intervals in ascending order: [iv[0], iv[1]] and, when two
+// are returned, [iv[2], iv[3]]. The window [f - wb, f + wa] is clamped to
+// [0, F - 1]; the span of reference frames is merged into it when they
+// overlap or touch.
+__host__ __device__ inline int live_intervals(const LiveGeom &g, int f, int iv[4]) {
+  if (g.rg && f >= g.r && f < g.r + g.nr) {
+    iv[0] = 0;
+    iv[1] = g.F - 1;
+    return 1;
+  }
+  const int64_t l = (int64_t)f - g.wb, h = (int64_t)f + g.wa;   // (windows may be wider than F)
+  const int lo = l < 0 ? 0 : (int)l, hi = h > g.F - 1 ? g.F - 1 : (int)h;
+  iv[0] = lo;
+  iv[1] = hi;
+  if (g.nr == 0) return 1;
+  const int ra = g.r, rb = g.r + g.nr - 1;
+  if (ra <= hi + 1 && rb >= lo - 1) {
+    iv[0] = ra < lo ? ra : lo;
+    iv[1] = rb > hi ? rb : hi;
+    return 1;
+  }
+  if (rb < lo) {
+    iv[0] = ra; iv[1] = rb; iv[2] = lo; iv[3] = hi;
+  } else {
+    iv[2] = ra; iv[3] = rb;
+  }
+  return 2;
+}
+
 // Host-side geometry helpers (fsattn_plan.cpp).
 bool geometry_ok(const fsattn_mask *m);
 // Live frames of query frame f in ascending order; returns the count.
@@ -22,8 +70,7 @@ struct BoundsParams {
   const void *q, *k;
   int64_t qsb, qsh, qsn, ksb, ksh, ksn;
   int B, H, N, F, T, D;
-  int wr, wa, ref;              // window and reference frame
-  int ref_global;               // the reference frame's queries see every frame
+  LiveGeom live;                 // window and reference frames
   int chunk, chunks_per_frame;  // token chunk (within one frame)
   float scale, threshold;
   float *key_mean;

@@ -2,9 +2,10 @@
 // Bringing Avatar IV to TPUs", section "Deleting the Mask", Fig. 3).
 //
 // Query frame f sees the key frames of the clamped window
-// [f - window_before, f + window_after] plus the reference frame; with
-// ref_queries_global the reference frame's own queries see every frame.
-// With block sizes that are multiples of 16 dividing the frame span, a (query block,
+// [f - window_before, f + window_after] plus the reference frames (ref_count
+// consecutive frames from ref_frame); with ref_queries_global the reference
+// frames' own queries see every frame. With block sizes that are multiples
+// of 16 dividing the frame span, a (query block,
 // key block) pair is live exactly when the key block's frame is live for
 // the query block's frame, and then every token pair in it is live. So the
 // plan is a frame-level list expanded to blocks: each query block of frame
@@ -26,55 +27,37 @@ bool geometry_ok(const fsattn_mask *m) {
   if (m->window_before < 0 || m->window_after < 0) return false;
   if (m->ref_frame < -1 || m->ref_frame >= F) return false;
   if (m->ref_queries_global != 0 && m->ref_queries_global != 1) return false;
+  if (m->ref_count < 0) return false;
+  if (m->ref_frame >= 0 && (int64_t)m->ref_frame + std::max(1, m->ref_count) > F) return false;
   for (int64_t b : {(int64_t)m->block_q, (int64_t)m->block_k})
     if (b <= 0 || b % 16 != 0 || T % b != 0) return false;
   return true;
 }
 
-static void window_of(const fsattn_mask *m, int f, int *lo, int *hi) {
-  if (m->ref_queries_global && m->ref_frame >= 0 && f == m->ref_frame) {
-    *lo = 0;   // a global reference frame's queries see every frame
-    *hi = m->num_frames - 1;
-    return;
-  }
-  const int64_t l = std::max<int64_t>(0, (int64_t)f - m->window_before);
-  const int64_t h = std::min<int64_t>((int64_t)m->num_frames - 1, (int64_t)f + m->window_after);
-  *lo = (int)l;
-  *hi = (int)h;
-}
-
 int64_t live_frame_count(const fsattn_mask *m, int f) {
-  int lo, hi;
-  window_of(m, f, &lo, &hi);
-  int64_t n = hi - lo + 1;
-  if (m->ref_frame >= 0 && (m->ref_frame < lo || m->ref_frame > hi)) n += 1;
-  return n;
+  int iv[4];
+  const int n = live_intervals(live_geom(*m), f, iv);
+  int64_t c = 0;
+  for (int i = 0; i < n; ++i) c += iv[2 * i + 1] - iv[2 * i] + 1;
+  return c;
 }
 
 int live_frames(const fsattn_mask *m, int f, int *out, int cap) {
-  int lo, hi;
-  window_of(m, f, &lo, &hi);
-  const int r = m->ref_frame;
-  int n = 0;
-  auto put = [&](int x) { if (n < cap) out[n] = x; n++; };
-  if (r >= 0 && r < lo) put(r);
-  for (int g = lo; g <= hi; ++g) put(g);
-  if (r >= 0 && r > hi) put(r);
-  return n;
+  int iv[4];
+  const int n = live_intervals(live_geom(*m), f, iv);
+  int c = 0;
+  for (int i = 0; i < n; ++i)
+    for (int g = iv[2 * i]; g <= iv[2 * i + 1]; ++g, ++c)
+      if (c < cap) out[c] = g;
+  return c;
 }
 
 int max_runs_per_frame(const fsattn_mask *m) {
-  // The window is one contiguous frame range; the reference frame adds a
-  // second run unless it is inside or adjacent to the window.
-  int best = 0;
-  for (int f = 0; f < m->num_frames; ++f) {
-    int lo, hi;
-    window_of(m, f, &lo, &hi);
-    const int r = m->ref_frame;
-    int runs = 1;
-    if (r >= 0 && (r < lo - 1 || r > hi + 1)) runs = 2;
-    best = std::max(best, runs);
-  }
+  // The window is one contiguous frame range; the span of reference frames
+  // adds a second run unless it overlaps or touches the window.
+  const LiveGeom g = live_geom(*m);
+  int best = 0, iv[4];
+  for (int f = 0; f < m->num_frames; ++f) best = std::max(best, live_intervals(g, f, iv));
   return best;
 }
 
@@ -104,25 +87,19 @@ extern "C" fsattn_status fsattn_plan(const fsattn_mask *m, int32_t *row_ptr, int
   if (row_ptr_len < nqb + 1 || col_idx_len < nnz) return FSATTN_ERR_BUFFER_TOO_SMALL;
   const int T = m->tokens_per_frame;
   const int qpf = T / m->block_q, kpf = T / m->block_k;
-  int frames[4096];
+  const LiveGeom g = live_geom(*m);
   int64_t pos = 0;
   int64_t qb = 0;
   row_ptr[0] = 0;
   for (int f = 0; f < m->num_frames; ++f) {
-    const int n = live_frames(m, f, frames, 4096);
+    int iv[4];
+    const int n = live_intervals(g, f, iv);
     for (int i = 0; i < qpf; ++i) {
-      if (n <= 4096) {
-        for (int j = 0; j < n; ++j)
-          for (int c = 0; c < kpf; ++c) col_idx[pos++] = frames[j] * kpf + c;
-      } else {  // very wide windows: enumerate frames directly, same order
-        int lo, hi;
-        window_of(m, f, &lo, &hi);
-        const int r = m->ref_frame;
-        auto emit = [&](int g) { for (int c = 0; c < kpf; ++c) col_idx[pos++] = g * kpf + c; };
-        if (r >= 0 && r < lo) emit(r);
-        for (int g = lo; g <= hi; ++g) emit(g);
-        if (r >= 0 && r > hi) emit(r);
-      }
+      // the live frames' key blocks, ascending: each interval of frames is
+      // one contiguous range of key blocks
+      for (int j = 0; j < n; ++j)
+        for (int64_t c = (int64_t)iv[2 * j] * kpf; c < (int64_t)(iv[2 * j + 1] + 1) * kpf; ++c)
+          col_idx[pos++] = (int32_t)c;
       row_ptr[++qb] = (int32_t)pos;
     }
   }

@@ -60,7 +60,7 @@ double list_finish(const std::vector<double> &cost, int S) {
   return *std::max_element(t.begin(), t.end());
 }
 
-using Key = std::tuple<int, int, int, int, int, int, int, int, int, int>;
+using Key = std::tuple<int, int, int, int, int, int, int, int, int, int, int>;
 std::mutex g_mu;
 std::map<Key, int> g_cache;
 
@@ -83,7 +83,7 @@ int choose_deal_chunk(const fsattn_shape *s, const fsattn_mask *m, const FwdConf
   if (G > kMaxRounds * kXcds * S) return TPF;
 
   const Key key{m->num_frames, m->tokens_per_frame, m->window_before, m->window_after, m->ref_frame,
-                m->ref_queries_global, BH, rows, s->head_dim, S};
+                m->ref_queries_global, m->ref_count, BH, rows, s->head_dim, S};
   {
     std::lock_guard<std::mutex> lock(g_mu);
     auto it = g_cache.find(key);

@@ -3,8 +3,8 @@
 // host plan, element for element, straight into device memory.
 //
 // Query frame f sees the key frames of the clamped window
-// [f - window_before, f + window_after] plus the reference frame (all frames
-// for a global reference frame's own queries), so every
+// [f - window_before, f + window_after] plus the reference frames (all
+// frames for the queries of global reference frames), so every
 // query block of frame f lists the same key blocks: those of its live
 // frames, ascending. One workgroup per query frame finds where the frame's
 // rows start (the sum of the earlier frames' row lengths), then writes its
@@ -20,20 +20,15 @@ namespace {
 constexpr int kPlanThreads = 256;
 
 struct PlanGeom {
-  int F, wb, wa, ref, ref_global, qpf, kpf;
+  LiveGeom live;
+  int qpf, kpf;
 };
 
-// Live frames of query frame f: the clamped window [lo, hi], plus the
-// reference frame before (extra = -1) or after (extra = +1) it, or none
-// (extra = 0) when there is no reference frame or it lies in the window.
-__device__ inline void live_of(const PlanGeom &g, int f, int &lo, int &hi, int &extra) {
-  const bool all = g.ref_global && f == g.ref;
-  const int64_t l = (int64_t)f - g.wb, h = (int64_t)f + g.wa;   // (windows may be wider than F)
-  lo = all || l < 0 ? 0 : (int)l;
-  hi = all || h > g.F - 1 ? g.F - 1 : (int)h;
-  extra = 0;
-  if (g.ref >= 0 && g.ref < lo) extra = -1;
-  if (g.ref >= 0 && g.ref > hi) extra = 1;
+// Number of frames in the live intervals of query frame f.
+__device__ inline int live_count(const LiveGeom &g, int f, int iv[4], int *first) {
+  const int n = live_intervals(g, f, iv);
+  *first = iv[1] - iv[0] + 1;
+  return n == 1 ? *first : *first + iv[3] - iv[2] + 1;
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanGeom g, int32_t *row_ptr, int32_t *col_idx) {
@@ -44,9 +39,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanGeom g, int32_t 
   // blocks per frame pair
   int64_t before = 0;
   for (int h = t; h < f; h += kPlanThreads) {
-    int lo, hi, extra;
-    live_of(g, h, lo, hi, extra);
-    before += (int64_t)(hi - lo + 1 + (extra != 0));
+    int iv[4], first;
+    before += live_count(g.live, h, iv, &first);
   }
   part[t] = before;
   __syncthreads();
@@ -55,9 +49,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanGeom g, int32_t 
     __syncthreads();
   }
   const int64_t base = part[0] * g.qpf * g.kpf;
-  int lo, hi, extra;
-  live_of(g, f, lo, hi, extra);
-  const int n = hi - lo + 1 + (extra != 0);
+  int iv[4], first;
+  const int n = live_count(g.live, f, iv, &first);
   const int E = n * g.kpf;   // entries per query block of this frame
   if (f == 0 && t == 0) row_ptr[0] = 0;
   for (int i = t; i < g.qpf; i += kPlanThreads)
@@ -66,10 +59,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanGeom g, int32_t 
   for (int64_t idx = t; idx < total; idx += kPlanThreads) {
     const int e = (int)(idx % E);
     const int j = e / g.kpf, c = e % g.kpf;   // j-th live frame, its c-th key block
-    int frame;
-    if (extra < 0) frame = j == 0 ? g.ref : lo + j - 1;
-    else if (extra > 0) frame = j == n - 1 ? g.ref : lo + j;
-    else frame = lo + j;
+    const int frame = j < first ? iv[0] + j : iv[2] + (j - first);
     col_idx[base + idx] = frame * g.kpf + c;
   }
 }
@@ -78,14 +68,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanGeom g, int32_t 
 
 hipError_t launch_plan_device(const fsattn_mask &m, int32_t *row_ptr, int32_t *col_idx, hipStream_t st) {
   PlanGeom g;
-  g.F = m.num_frames;
-  g.wb = m.window_before;
-  g.wa = m.window_after;
-  g.ref = m.ref_frame;
-  g.ref_global = m.ref_queries_global;
+  g.live = live_geom(m);
   g.qpf = m.tokens_per_frame / m.block_q;
   g.kpf = m.tokens_per_frame / m.block_k;
-  hipLaunchKernelGGL(plan_kernel, dim3(g.F), dim3(kPlanThreads), 0, st, g, row_ptr, col_idx);
+  hipLaunchKernelGGL(plan_kernel, dim3(g.live.F), dim3(kPlanThreads), 0, st, g, row_ptr, col_idx);
   return hipGetLastError();
 }
 

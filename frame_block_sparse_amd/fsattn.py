@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libfsattn.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fsattn.h")
 
 # the layout of the structures below (FSATTN_ABI_VERSION of the header)
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 F32, BF16 = 0, 1
 MODE_AUTO, MODE_FORCE_ONLINE, MODE_FORCE_FIXED, SHIFT_PER_ROW = 0, 1, 2, 4
@@ -34,7 +34,7 @@ class Mask(ctypes.Structure):
     _fields_ = [("num_frames", ctypes.c_int32), ("tokens_per_frame", ctypes.c_int32),
                 ("window_before", ctypes.c_int32), ("window_after", ctypes.c_int32),
                 ("ref_frame", ctypes.c_int32), ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32),
-                ("ref_queries_global", ctypes.c_int32)]
+                ("ref_queries_global", ctypes.c_int32), ("ref_count", ctypes.c_int32)]
 
 
 class Shape(ctypes.Structure):
@@ -127,16 +127,17 @@ def _check(st: int, what: str):
 
 
 def to_mask(mask) -> Mask:
-    """A Mask from a Mask, a 7- or 8-tuple (num_frames, tokens_per_frame,
-    window_before, window_after, ref_frame, block_q, block_k
-    [, ref_queries_global]) or any object with a mask_tuple() method."""
+    """A Mask from a Mask, a tuple of 7 to 9 integers (num_frames,
+    tokens_per_frame, window_before, window_after, ref_frame, block_q,
+    block_k [, ref_queries_global [, ref_count]]) or any object with a
+    mask_tuple() method."""
     if isinstance(mask, Mask):
         return mask
     if hasattr(mask, "mask_tuple"):
         mask = mask.mask_tuple()
     vals = [int(x) for x in mask]
-    if len(vals) not in (7, 8):
-        raise ValueError(f"a mask has 7 or 8 integers, got {len(vals)}")
+    if len(vals) not in (7, 8, 9):
+        raise ValueError(f"a mask has 7 to 9 integers, got {len(vals)}")
     return Mask(*vals)
 
 

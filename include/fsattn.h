@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define FSATTN_ABI_VERSION 2
+#define FSATTN_ABI_VERSION 3
 
 typedef enum fsattn_status {
   FSATTN_OK = 0,
@@ -56,17 +56,20 @@ enum { FSATTN_F32 = 0, FSATTN_BF16 = 1 };
  * The frame-structured mask and its block tiling ("Deleting the Mask",
  * Fig. 3). Query frame f sees the key frames of the window
  * [f - window_before, f + window_after] clamped to [0, num_frames - 1],
- * plus frame ref_frame (-1: no reference frame). block_q and block_k must
+ * plus the reference frames: ref_count consecutive frames from ref_frame
+ * (ref_frame -1: none; ref_count 0 or 1: the one frame ref_frame; the span
+ * must end inside the sequence). block_q and block_k must
  * be positive multiples of 16 that divide tokens_per_frame, so that every
  * block is entirely live or entirely masked.
  *
- * ref_queries_global (0 or 1) widens the reference frame to a global token
+ * ref_queries_global (0 or 1) widens the reference frames to global tokens
  * in both directions, the symmetric reading of a "global" frame: with 1,
- * the reference frame's own queries see every key frame, instead of only
+ * the reference frames' own queries see every key frame, instead of only
  * their window. The section describes the reference frame only as keys
  * every frame attends to, so 0 (keys only) is the default reading. Without
- * a reference frame (ref_frame = -1) the field has no effect. Any other
- * value is a geometry error.
+ * a reference frame (ref_frame = -1) ref_queries_global and ref_count have
+ * no effect. Other values (ref_queries_global not 0 or 1, a negative
+ * ref_count, a span past the last frame) are geometry errors.
  */
 typedef struct fsattn_mask {
   int32_t num_frames;
@@ -77,6 +80,7 @@ typedef struct fsattn_mask {
   int32_t block_q;
   int32_t block_k;
   int32_t ref_queries_global;
+  int32_t ref_count;
 } fsattn_mask;
 
 /* Problem shape. seq_len must equal num_frames * tokens_per_frame.
@@ -257,8 +261,8 @@ fsattn_status fsattn_forward_launch_info(const fsattn_shape *s, const fsattn_mas
  * normalised fp32 rows and log-sum-exps to the workspace, and a third kernel
  * merges them into o. bf16 inputs only (same MFMA, LDS staging and copies as
  * fsattn_forward's default launch); block_q/block_k of the mask are not
- * used, and a global reference frame (ref_queries_global = 1) is
- * UNSUPPORTED. workspace: DEVICE memory, 16-byte aligned, >=
+ * used, and global reference frames (ref_queries_global = 1) or more than
+ * one reference frame (ref_count > 1) are UNSUPPORTED. workspace: DEVICE memory, 16-byte aligned, >=
  * fsattn_prior_art_workspace_bytes(). Asynchronous on hip_stream.
  * Errors: INVALID_ARGUMENT, BLOCK_GEOMETRY, UNSUPPORTED, BUFFER_TOO_SMALL,
  * HIP.

@@ -23,11 +23,11 @@ def test_library_loads_and_exports_every_declared_symbol():
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
     for n in names:
         assert n in exported, n
-    assert fs.abi_version() == F.ABI_VERSION == 2
+    assert fs.abi_version() == F.ABI_VERSION == 3
 
 
 def test_struct_layouts():
-    assert ctypes.sizeof(F.Mask) == 32
+    assert ctypes.sizeof(F.Mask) == 36
     assert ctypes.sizeof(F.Shape) == 20
     assert ctypes.sizeof(F.Tensor) == 32
     assert ctypes.sizeof(F.HeadBound) == 32
@@ -50,7 +50,9 @@ def test_plan_bit_exact_vs_oracle_random_geometries():
         divs = [b for b in range(16, T + 1, 16) if T % b == 0]
         Fn = int(rng.integers(1, 12))
         t = (Fn, T, int(rng.integers(0, 5)), int(rng.integers(0, 5)), int(rng.integers(-1, Fn)),
-             int(rng.choice(divs)), int(rng.choice(divs)), int(rng.integers(0, 2)))
+             int(rng.choice(divs)), int(rng.choice(divs)), int(rng.integers(0, 2)), int(rng.integers(0, 4)))
+        if t[4] + max(1, t[8]) > Fn:
+            t = t[:8] + (0,)
         rp, ci = fs.plan(t)
         orp, oci = oracle.plan_bruteforce(oracle.MaskGeometry(*t))
         assert np.array_equal(rp.numpy(), orp), t
@@ -69,7 +71,8 @@ def test_plan_golden():
     ((3, 48, 1, 1, 0, 32, 16), 2), ((3, 48, 1, 1, 0, 24, 16), 2), ((3, 48, 1, 1, 0, 16, 0), 2),
     ((3, 48, -1, 1, 0, 16, 16), 2), ((3, 48, 1, 1, 3, 16, 16), 2), ((3, 48, 1, 1, -2, 16, 16), 2),
     ((0, 48, 1, 1, -1, 16, 16), 2), ((3, 40, 1, 1, 0, 16, 16), 2), ((3, 48, 1, 1, 0, 16, 16, 2), 2),
-    ((3, 48, 1, 1, 0, 16, 16, -1), 2)])
+    ((3, 48, 1, 1, 0, 16, 16, -1), 2), ((3, 48, 1, 1, 2, 16, 16, 0, 2), 2), ((3, 48, 1, 1, 0, 16, 16, 0, -1), 2),
+    ((3, 48, 1, 1, 0, 16, 16, 0, 4), 2)])
 def test_plan_rejects_bad_geometry(mask, status):
     with pytest.raises(fs.FsattnError) as e:
         fs.plan_size(mask)
@@ -228,6 +231,7 @@ def test_prior_art_forward_validates_on_host():
     assert call(scale=0.0) == 1
     assert call(shape=F.Shape(1, 2, 241, 64, 1)) == 1      # seq_len != F*T
     assert L.fsattn_prior_art_workspace_bytes(ctypes.byref(F.Shape(1, 2, 240, 64, 0)), ctypes.byref(m)) == 0
-    mg = F.to_mask((5, 48, 1, 1, 0, 16, 16, 1))            # the comparator has no global reference frame
-    assert L.fsattn_prior_art_forward(None, ctypes.byref(s), ctypes.byref(mg), _t(), _t(), _t(), _t(), 1,
-                                      0.125, FAKE, need) == 3
+    for t in ((5, 48, 1, 1, 0, 16, 16, 1), (5, 48, 1, 1, 0, 16, 16, 0, 2)):   # one keys-only reference frame
+        mg = F.to_mask(t)
+        assert L.fsattn_prior_art_forward(None, ctypes.byref(s), ctypes.byref(mg), _t(), _t(), _t(), _t(), 1,
+                                          0.125, FAKE, need) == 3

@@ -90,13 +90,15 @@ def test_plan_device_bit_exact_on_workloads(dev, i):
 def test_plan_device_bit_exact_on_random_geometries(dev):
     rng = np.random.default_rng(11)
     cases = [(3, 32, 10 ** 6, 10 ** 6, 1, 16, 32), (1, 16, 0, 0, -1, 16, 16), (7, 48, 0, 2, 6, 48, 16),
-             (7, 48, 0, 2, 6, 48, 16, 1), (9, 32, 1, 1, 4, 16, 32, 1)]
+             (7, 48, 0, 2, 6, 48, 16, 1), (9, 32, 1, 1, 4, 16, 32, 1), (9, 32, 1, 1, 4, 16, 32, 0, 3),
+             (9, 32, 0, 0, 0, 32, 16, 1, 2), (6, 16, 10 ** 6, 0, 3, 16, 16, 0, 3)]
     for _ in range(40):
         T = 16 * int(rng.integers(1, 7))
         divs = [b for b in range(16, T + 1, 16) if T % b == 0]
         F_ = int(rng.integers(1, 12))
-        cases.append((F_, T, int(rng.integers(0, 4)), int(rng.integers(0, 4)), int(rng.integers(-1, F_)),
-                      int(rng.choice(divs)), int(rng.choice(divs)), int(rng.integers(0, 2))))
+        t = (F_, T, int(rng.integers(0, 4)), int(rng.integers(0, 4)), int(rng.integers(-1, F_)),
+             int(rng.choice(divs)), int(rng.choice(divs)), int(rng.integers(0, 2)), int(rng.integers(0, 4)))
+        cases.append(t if t[4] + max(1, t[8]) <= F_ else t[:8] + (0,))
     for g in cases:
         rp, ci = fs.plan(g)
         dp = fs.plan_on_device(g, dev)
@@ -313,23 +315,27 @@ def test_forward_workload_parity(dev, config_inputs, i):
     assert np.all(np.abs(o) <= vmax * (1 + 2 ** -7) + 1e-6)
 
 
-# The reference frame as a global token in both directions: its own queries
-# see every frame (mask option ref_queries_global).
-GLOBAL_REF = [
-    # (name, B, H, F, T, d, dtype, wb, wa, ref, bq, bk)
-    ("gref_mid", 1, 2, 6, 160, 128, "bf16", 1, 1, 2, 32, 32),
-    ("gref0_d64", 2, 2, 5, 96, 64, "bf16", 0, 0, 0, 48, 16),
-    ("gref_last_tail", 1, 3, 4, 240, 128, "bf16", 1, 0, 3, 48, 80),
-    ("gref_f32", 1, 2, 4, 80, 128, "f32", 1, 0, 3, 16, 80),
+# Mask variants: the reference frames as global tokens in both directions
+# (their own queries see every frame), and spans of several reference frames.
+MASK_VARIANTS = [
+    # (name, B, H, F, T, d, dtype, wb, wa, ref, bq, bk, ref_queries_global, ref_count)
+    ("gref_mid", 1, 2, 6, 160, 128, "bf16", 1, 1, 2, 32, 32, 1, 0),
+    ("gref0_d64", 2, 2, 5, 96, 64, "bf16", 0, 0, 0, 48, 16, 1, 0),
+    ("gref_last_tail", 1, 3, 4, 240, 128, "bf16", 1, 0, 3, 48, 80, 1, 0),
+    ("gref_f32", 1, 2, 4, 80, 128, "f32", 1, 0, 3, 16, 80, 1, 0),
+    ("span2_mid", 1, 2, 7, 160, 128, "bf16", 1, 1, 3, 32, 32, 0, 2),
+    ("span3_first_gref", 1, 2, 8, 96, 128, "bf16", 0, 1, 0, 48, 16, 1, 3),
+    ("span2_last_d64", 2, 1, 6, 112, 64, "bf16", 1, 0, 4, 16, 112, 0, 2),
+    ("span2_f32", 1, 2, 5, 80, 64, "f32", 1, 0, 2, 16, 80, 0, 2),
 ]
 
 
-@pytest.mark.parametrize("case", GLOBAL_REF, ids=[c[0] for c in GLOBAL_REF])
+@pytest.mark.parametrize("case", MASK_VARIANTS, ids=[c[0] for c in MASK_VARIANTS])
 @pytest.mark.parametrize("mode", ["auto", "online", "fixed"])
-def test_forward_global_reference_frame_parity(dev, case, mode):
-    w, q, k, v = _small(case, seed=4, key_offset=1.5)
-    w = dataclasses.replace(w, ref_queries_global=1)
-    _say(f"[fwd-gref] {w.name} mode={mode}")
+def test_forward_mask_variant_parity(dev, case, mode):
+    w, q, k, v = _small(case[:12], seed=4, key_offset=1.5)
+    w = dataclasses.replace(w, ref_queries_global=case[12], ref_count=case[13])
+    _say(f"[fwd-variant] {w.name} mode={mode}")
     out, bnd, lse = _run(w, q, k, v, dev, flags=fs.make_flags(mode), lse=True)
     g = _geom(w)
     rec = oracle.head_bounds_ref(q, k, g)
@@ -342,12 +348,14 @@ def test_forward_global_reference_frame_parity(dev, case, mode):
     assert lerr <= LSE_TOL[w.dtype], lerr
 
 
-def test_forward_global_reference_frame_full_size(dev, config_inputs):
-    """21 frames x 960 tokens with a global reference frame 0, in the
-    library's default launch: bounds against the oracle, and sampled rows of
-    every frame (frame 0's rows see all 20,160 keys) against it."""
-    w = dataclasses.replace(workloads.config(2), ref_queries_global=1)
-    _say(f"[fwd-gref] {w.name} + global reference frame")
+@pytest.mark.parametrize("variant", [(1, 0), (0, 2), (1, 3)], ids=["global_ref", "span2", "global_span3"])
+def test_forward_mask_variant_full_size(dev, config_inputs, variant):
+    """21 frames x 960 tokens with a global reference frame 0 (its rows see
+    all 20,160 keys), with reference frames 0-1, and with global reference
+    frames 0-2, in the library's default launch: bounds against the oracle,
+    and sampled rows of every frame against it."""
+    w = dataclasses.replace(workloads.config(2), ref_queries_global=variant[0], ref_count=variant[1])
+    _say(f"[fwd-variant] {w.name} ref_queries_global={variant[0]} ref_count={variant[1]}")
     q, k, v = config_inputs(2)
     out, bnd, _ = _run(w, q, k, v, dev)
     g = _geom(w)

@@ -43,7 +43,8 @@ class Workload:
     block_k: int
     modifier: str = "none"   # none | scale_qk | key_offset | stress_keys | rmsnorm_qk
     description: str = ""
-    ref_queries_global: int = 0   # 1: the reference frame's queries see every frame
+    ref_queries_global: int = 0   # 1: the reference frames' queries see every frame
+    ref_count: int = 0            # reference frames from ref_frame (0 or 1: one)
 
     @property
     def seq_len(self) -> int:
@@ -51,11 +52,11 @@ class Workload:
 
     def mask_tuple(self):
         """(num_frames, tokens_per_frame, window_before, window_after,
-        ref_frame, block_q, block_k, ref_queries_global) - the eight
-        integers of the mask descriptor, in the C struct's field order."""
+        ref_frame, block_q, block_k, ref_queries_global, ref_count) - the
+        nine integers of the mask descriptor, in the C struct's field order."""
         return (self.num_frames, self.tokens_per_frame, self.window_before,
                 self.window_after, self.ref_frame, self.block_q, self.block_k,
-                self.ref_queries_global)
+                self.ref_queries_global, self.ref_count)
 
 
 # The five workloads. Sizes are one GPU's share of heads at the full
@@ -89,11 +90,12 @@ def config(i: int) -> Workload:
 def make_workload(name, batch, heads, num_frames, tokens_per_frame, head_dim,
                   dtype="bf16", window_before=1, window_after=1, ref_frame=0,
                   block_q=16, block_k=16, modifier="none",
-                  ref_queries_global=0) -> Workload:
+                  ref_queries_global=0, ref_count=0) -> Workload:
     """A custom (test-sized) workload with the same recipe."""
     return Workload(name, batch, heads, num_frames, tokens_per_frame, head_dim,
                     dtype, window_before, window_after, ref_frame, block_q,
-                    block_k, modifier, ref_queries_global=ref_queries_global)
+                    block_k, modifier, ref_queries_global=ref_queries_global,
+                    ref_count=ref_count)
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
