@@ -7,4 +7,5 @@ from .fsattn_oracle import (MaskGeometry, live_frames, token_mask, row_mask, mas
                             plan_bruteforce, attention_ref, attention_online_ref,
                             attention_fixed_shift_ref, head_bounds_ref, row_shift_ref,
                             live_logit_stats, live_flops, partial_blocks_if_tiled,
+                            rms_norm_ref, rope_ref, produce_ref, rope_tables_1d, producer_bytes,
                             GAP_THRESHOLD_NATS)

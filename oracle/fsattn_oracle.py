@@ -20,6 +20,11 @@ Developers Blog; a paraphrased copy carries the section headings used below).
     is too loose use the online softmax; the bound's guarantee is extended to
     windowed masks where each query row sees a different slice of keys.
 
+  * "Layout Is the ABI", Fig. 5: the small operations that produce
+    attention's inputs (normalisation, rotary embeddings, projections,
+    head packing) are fused into one kernel that writes the layout its
+    consumer reads.
+
 Because blocks are exactly full or empty and a softmax is invariant under a
 per-row shift, the method's output is, up to rounding, plain softmax
 attention under the token-level mask. So the attention oracle is that plain
@@ -49,6 +54,13 @@ Readings where the pages are silent (each also listed in the design notes):
       where C_max = max_f |mean of the keys live for frame f - mu_h|; this
       upper-bounds "bound minus logit max" for every row, so it can be
       checked before any logit is computed.
+  R14 the fused chain: per-head RMSNorm over d with a gamma per (head,
+      dimension), then the rotary embedding, on Q and K; V is only moved.
+      The projection is a plain GEMM left to the caller; its output is the
+      chain's input, read through strides
+  R15 rotary embedding: RoFormer's rotation of dimension pairs (2i, 2i+1),
+      with per-token angle tables supplied by the caller (1-D or
+      multi-axis positions alike)
 
 Parity status: every function below is pinned by tests that do not reuse
 its own arithmetic (brute force over tokens, closed forms, invariants,
@@ -363,3 +375,62 @@ def live_flops(g: MaskGeometry, batch: int, heads: int, head_dim: int) -> int:
     pairs only, 2*d flops each: 4 * d * B * H * sum_f |L(f)| * T^2."""
     pairs = sum(len(live_frames(g, f)) for f in range(g.F)) * g.T * g.T
     return 4 * head_dim * batch * heads * pairs
+
+
+# ---------------------------------------------------------------- producer
+
+def rms_norm_ref(x, gamma, eps):
+    """Per-row RMS normalisation over the last axis (the "normalization" of
+    the chain that produces attention's inputs, "Layout Is the ABI"):
+    y = gamma * x / sqrt(mean(x^2) + eps). x: (B, H, N, d); gamma: (H, d)
+    or None (no normalisation). R14."""
+    x = np.asarray(x, dtype=np.float64)
+    if gamma is None:
+        return x.copy()
+    r = np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + float(eps))
+    return np.asarray(gamma, dtype=np.float64)[None, :, None, :] * (x / r)
+
+
+def rope_ref(x, cos, sin):
+    """Rotary position embedding (the "rotary embeddings" of the same chain),
+    RoFormer's form: dimension pair (2i, 2i+1) of token n is rotated by the
+    angle whose cosine and sine are cos[n, i] and sin[n, i]:
+        y[2i]   = x[2i] cos - x[2i+1] sin
+        y[2i+1] = x[2i] sin + x[2i+1] cos.
+    The caller's tables carry the positional scheme (R15). x: (B, H, N, d);
+    cos, sin: (N, d/2) or None (no rotation)."""
+    x = np.asarray(x, dtype=np.float64)
+    if cos is None:
+        return x.copy()
+    c = np.asarray(cos, dtype=np.float64)[None, None]
+    s = np.asarray(sin, dtype=np.float64)[None, None]
+    y = np.empty_like(x)
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    y[..., 0::2] = x0 * c - x1 * s
+    y[..., 1::2] = x0 * s + x1 * c
+    return y
+
+
+def produce_ref(q_in, k_in, v_in, gamma_q=None, gamma_k=None, eps=1e-6, cos=None, sin=None):
+    """The chain that produces attention's inputs ("Layout Is the ABI",
+    Fig. 5), without its projection (R14): Q and K are RMS-normalised and
+    then rotated; V passes through. Inputs and outputs are (B, H, N, d) in
+    fp64; the layout the product writes is a matter of strides."""
+    q = rope_ref(rms_norm_ref(q_in, gamma_q, eps), cos, sin)
+    k = rope_ref(rms_norm_ref(k_in, gamma_k, eps), cos, sin)
+    return q, k, np.asarray(v_in, dtype=np.float64).copy()
+
+
+def rope_tables_1d(n, d, base=10000.0):
+    """RoFormer's tables for 1-D positions 0..n-1: angle n * base^(-2i/d)
+    for pair i. Returns (cos, sin), each (n, d/2) fp64."""
+    i = np.arange(d // 2, dtype=np.float64)
+    ang = np.arange(n, dtype=np.float64)[:, None] * base ** (-2.0 * i / d)[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
+def producer_bytes(batch, heads, seq_len, head_dim, elem_bytes):
+    """Algorithmic HBM bytes of one producer launch: Q, K and V read once and
+    written once (the per-head gammas and the angle tables are small and
+    not counted)."""
+    return 6 * batch * heads * seq_len * head_dim * elem_bytes

@@ -536,3 +536,117 @@ def test_planted_mistake_missing_scale_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "attention_ref", unscaled)
     assert _run_pins_quietly([lambda: test_attention_matches_bruteforce_loops((3, 4, 1, 1, 0)),
                               test_attention_dense_matches_torch_sdpa]) == 2
+
+
+# ------------------------------------------------------------------ producer (norm + rotary + layout)
+
+def test_rope_hand_examples():
+    # d = 4, x = (1, 2, 3, 4): pair 0 is (1, 2), pair 1 is (3, 4)
+    x = np.array([1.0, 2.0, 3.0, 4.0]).reshape(1, 1, 1, 4)
+    def rot(a0, a1):
+        c = np.array([[math.cos(a0), math.cos(a1)]])
+        s = np.array([[math.sin(a0), math.sin(a1)]])
+        return oracle.rope_ref(x, c, s).ravel()
+    np.testing.assert_allclose(rot(math.pi / 2, 0.0), [-2, 1, 3, 4], atol=1e-15)
+    np.testing.assert_allclose(rot(0.0, math.pi / 2), [1, 2, -4, 3], atol=1e-15)
+    np.testing.assert_allclose(rot(math.pi, math.pi), [-1, -2, -3, -4], atol=1e-15)
+    np.testing.assert_allclose(rot(0.0, 0.0), [1, 2, 3, 4], atol=0)
+
+
+def test_rope_matches_complex_multiplication():
+    rng = np.random.default_rng(30)
+    x = rng.standard_normal((2, 3, 7, 16))
+    ang = rng.uniform(-4, 4, (7, 8))
+    y = oracle.rope_ref(x, np.cos(ang), np.sin(ang))
+    z = (x[..., 0::2] + 1j * x[..., 1::2]) * np.exp(1j * ang)[None, None]
+    np.testing.assert_allclose(y[..., 0::2], z.real, atol=1e-13)
+    np.testing.assert_allclose(y[..., 1::2], z.imag, atol=1e-13)
+
+
+def test_rope_preserves_norms_and_depends_on_relative_position():
+    rng = np.random.default_rng(31)
+    d, n = 8, 9
+    c, s = oracle.rope_tables_1d(n, d)
+    q = np.broadcast_to(rng.standard_normal(d), (1, 1, n, d)).copy()   # the same vector at every position
+    k = np.broadcast_to(rng.standard_normal(d), (1, 1, n, d)).copy()
+    rq, rk = oracle.rope_ref(q, c, s)[0, 0], oracle.rope_ref(k, c, s)[0, 0]
+    np.testing.assert_allclose(np.linalg.norm(rq, axis=1), np.linalg.norm(q[0, 0], axis=1), rtol=1e-14)
+    dots = rq @ rk.T                     # dots[m, j] depends on m - j only
+    for m in range(n):
+        for j in range(n):
+            if m >= 1 and j >= 1:
+                assert dots[m, j] == pytest.approx(dots[m - 1, j - 1], abs=1e-12)
+
+
+def test_rms_norm_matches_torch_and_closed_forms():
+    import torch
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((2, 3, 5, 16)) * 3
+    g = rng.uniform(0.5, 1.5, (3, 16))
+    y = oracle.rms_norm_ref(x, g, 1e-6)
+    for h in range(3):
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(x[:, h]), (16,), torch.from_numpy(g[h]), eps=1e-6)
+        np.testing.assert_allclose(y[:, h], ref.numpy(), rtol=1e-13, atol=1e-13)
+    # gamma = 1, eps = 0: every row has mean square 1
+    y1 = oracle.rms_norm_ref(x, np.ones((3, 16)), 0.0)
+    np.testing.assert_allclose(np.mean(y1 * y1, axis=-1), 1.0, rtol=1e-13)
+    # a constant row c: y = gamma * c / sqrt(c^2 + eps)
+    xc = np.full((1, 1, 1, 4), -2.0)
+    yc = oracle.rms_norm_ref(xc, np.array([[1.0, 2.0, 3.0, 4.0]]), 0.25)
+    np.testing.assert_allclose(yc.ravel(), np.array([1, 2, 3, 4]) * -2.0 / math.sqrt(4.25), rtol=1e-15)
+
+
+def test_produce_chain_order_and_pass_through():
+    rng = np.random.default_rng(33)
+    q, k, v = _rand_qkv(rng, 1, 2, 6, 8)
+    g = rng.uniform(0.5, 1.5, (2, 8))
+    c, s = oracle.rope_tables_1d(6, 8)
+    pq, pk, pv = oracle.produce_ref(q, k, v, g, g, 1e-6, c, s)
+    np.testing.assert_array_equal(pv, v)
+    # norm, then rotation: the rotation keeps each row's norm, which the
+    # normalisation fixed at ||gamma * x / rms(x)||
+    np.testing.assert_allclose(np.linalg.norm(pq, axis=-1), np.linalg.norm(oracle.rms_norm_ref(q, g, 1e-6), axis=-1),
+                               rtol=1e-13)
+    # rotating first and normalising second differs unless gamma is uniform
+    other = oracle.rms_norm_ref(oracle.rope_ref(q, c, s), g, 1e-6)
+    assert np.abs(other - pq).max() > 1e-3
+    # no gamma and no tables: the identity
+    for a, b in zip(oracle.produce_ref(q, k, v), (q, k, v)):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_planted_mistake_rotate_half_pairing_is_caught(monkeypatch):
+    def rotate_half(x, cos, sin):
+        x = np.asarray(x, dtype=np.float64)
+        h = x.shape[-1] // 2
+        c, s = np.asarray(cos)[None, None], np.asarray(sin)[None, None]
+        y = np.empty_like(x)
+        y[..., :h] = x[..., :h] * c - x[..., h:] * s
+        y[..., h:] = x[..., :h] * s + x[..., h:] * c
+        return y
+    monkeypatch.setattr(oracle, "rope_ref", rotate_half)
+    assert _run_pins_quietly([test_rope_hand_examples, test_rope_matches_complex_multiplication]) == 2
+
+
+def test_planted_mistake_rotation_sign_is_caught(monkeypatch):
+    real = O.rope_ref
+    def wrong_sign(x, cos, sin):
+        y = real(x, cos, sin)
+        x = np.asarray(x, dtype=np.float64)
+        y[..., 1::2] = -x[..., 0::2] * np.asarray(sin)[None, None] + x[..., 1::2] * np.asarray(cos)[None, None]
+        return y
+    monkeypatch.setattr(oracle, "rope_ref", wrong_sign)
+    assert _run_pins_quietly([test_rope_hand_examples, test_rope_matches_complex_multiplication,
+                              test_rope_preserves_norms_and_depends_on_relative_position]) == 3
+
+
+def test_planted_mistake_norm_without_eps_or_gamma_is_caught(monkeypatch):
+    def no_eps(x, gamma, eps):
+        x = np.asarray(x, dtype=np.float64)
+        return np.asarray(gamma)[None, :, None, :] * x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True))
+    def no_gamma(x, gamma, eps):
+        x = np.asarray(x, dtype=np.float64)
+        return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    for bad in (no_eps, no_gamma):
+        monkeypatch.setattr(oracle, "rms_norm_ref", bad)
+        assert _run_pins_quietly([test_rms_norm_matches_torch_and_closed_forms]) == 1
