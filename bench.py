@@ -135,6 +135,46 @@ def prior_art_timing(w, qd, kd, vd, fwd_ms: float, live_flops: float, reps: int 
                     "per-element frame predicates on partly live tiles, online softmax, fp32 (O, lse) merge"}
 
 
+def producer_timing(w, dev, bounds_ms: float, reps: int = 20):
+    """fsattn_produce at the workload's shape, from a token-major packed
+    projection output [B, N, 3, H, d]: RMSNorm(gamma) and rotary embedding of
+    Q and K, Q/K/V written head-major, and the bound records. Algorithmic
+    bytes: Q, K, V read and written once, plus the second read of K that the
+    key-norm maximum needs after the key mean (7 rows of d per token and
+    head). Reported beside the separate bounds call it replaces."""
+    import numpy as np
+    import torch
+    import frame_block_sparse_amd as fs
+    import workloads
+    x = workloads.make_producer_inputs(w, seed=1)
+    td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    qkv = torch.from_numpy(np.ascontiguousarray(
+        np.stack((x["q"], x["k"], x["v"]), axis=2).transpose(0, 3, 2, 1, 4))).to(td).to(dev)
+    views = [qkv[:, :, i].permute(0, 2, 1, 3) for i in range(3)]
+    gq, gk, cs, sn = (torch.from_numpy(x[n]).to(dev) for n in ("gamma_q", "gamma_k", "cos", "sin"))
+    B, H, N, d = views[0].shape
+    out = tuple(torch.empty((B, H, N, d), dtype=td, device=dev) for _ in range(3))
+    ws = torch.empty(max(1, fs.head_bounds_workspace_bytes(out[0], w)), dtype=torch.uint8, device=dev)
+    bnd = fs.Bounds(torch.empty((B, H, d), dtype=torch.float32, device=dev),
+                    torch.empty((B, H, 8), dtype=torch.float32, device=dev))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    fs.produce(*views, w, gq, gk, 1e-6, cs, sn, out=out, workspace=ws, bounds=bnd)
+    for a, b in ev:
+        a.record()
+        fs.produce(*views, w, gq, gk, 1e-6, cs, sn, out=out, workspace=ws, bounds=bnd)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    avg = sum(ms) / len(ms)
+    esz = 2 if w.dtype == "bf16" else 4
+    nbytes = 7.0 * B * H * N * d * esz
+    return {"avg_ms": round(avg, 5), "algorithmic_bytes": nbytes, "GBps": round(nbytes / (avg * 1e-3) / 1e9, 1),
+            "peak_GBps": PEAK_HBM_GBS, "frac": round(nbytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "separate_bounds_ms": round(bounds_ms, 5),
+            "what": "RMSNorm(gamma) + rotary embedding of Q, K from a token-major QKV projection output, "
+                    "Q/K/V written head-major, bound records of the values written (fsattn_produce)"}
+
+
 def cpu_baseline(w, q, k, v, budget_s: float):
     """fp64 oracle on a bounded sample of query rows (every frame, every
     head), timed on the host cores. Rate in live TFLOP/s."""
@@ -291,6 +331,7 @@ def main():
     ref_mfma = mfma_reference(dev) if w.dtype == "bf16" else None
     prior = prior_art_timing(w, qd, kd, vd, fwd_avg, live_flops) if w.dtype == "bf16" else None
     value = live_flops / (ms_step * 1e-3) / 1e12
+    producer = producer_timing(w, dev, bnd_avg)
     elig = bnd.host()["eligible"]
     esz = 2 if w.dtype == "bf16" else 4
     bounds_bytes = 2.0 * w.batch * w.heads * w.seq_len * w.head_dim * esz
@@ -332,6 +373,7 @@ def main():
         "plan": {"avg_ms": round(sum(plan_ms) / len(plan_ms), 5), "nnz": nnz},
         "bounds": {"avg_ms": round(bnd_avg, 5), "algorithmic_bytes": bounds_bytes,
                    "GBps": round(bounds_bytes / (bnd_avg * 1e-3) / 1e9, 1), "peak_GBps": PEAK_HBM_GBS},
+        "producer": producer,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle, bounded sample)", file=sys.stderr, flush=True)

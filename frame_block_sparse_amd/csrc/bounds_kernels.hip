@@ -4,7 +4,9 @@
 // term c_max of the bound audit for windowed masks, and eligibility.
 //
 // Four launches; the two passes stream Q and K (HBM-bound), the other two
-// are small:
+// are small. fsattn_produce runs the same four with the input-producing
+// chain ("Layout Is the ABI", Fig. 5) fused into pass 1, whose statistics
+// then come from the values it has just written:
 //   pass1   per (token chunk, head): partial key sums, partial max |q|^2
 //   head    per head: the frame key sums from their chunks, the key mean,
 //           c_max from the frame sums, max |q|
@@ -42,6 +44,49 @@ __device__ inline void load8<__hip_bfloat16>(const __hip_bfloat16 *p, float *x) 
   for (int i = 0; i < 4; ++i) {
     x[2 * i] = __uint_as_float(w[i] << 16);
     x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+// Round to the nearest bf16, ties to even (NaN stays NaN), and that value as
+// a float.
+__device__ inline uint32_t bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Store 8 values and return, in x, the values as stored.
+template <typename T>
+__device__ inline void store8(T *p, float *x);
+
+template <>
+__device__ inline void store8<float>(float *p, float *x) {
+  *reinterpret_cast<float4 *>(p) = float4{x[0], x[1], x[2], x[3]};
+  *reinterpret_cast<float4 *>(p + 4) = float4{x[4], x[5], x[6], x[7]};
+}
+
+template <>
+__device__ inline void store8<__hip_bfloat16>(__hip_bfloat16 *p, float *x) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = bf16_bits(x[2 * i]), hi = bf16_bits(x[2 * i + 1]);
+    w[i] = lo | (hi << 16);
+    x[2 * i] = __uint_as_float(lo << 16);
+    x[2 * i + 1] = __uint_as_float(hi << 16);
+  }
+  *reinterpret_cast<uint4 *>(p) = uint4{w[0], w[1], w[2], w[3]};
+}
+
+// Copy 8 elements unchanged.
+template <typename T>
+__device__ inline void copy8(const T *src, T *dst) {
+  if constexpr (sizeof(T) == 4) {
+    const float4 a = *reinterpret_cast<const float4 *>(src), b = *reinterpret_cast<const float4 *>(src + 4);
+    *reinterpret_cast<float4 *>(dst) = a;
+    *reinterpret_cast<float4 *>(dst + 4) = b;
+  } else {
+    *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
   }
 }
 
@@ -89,8 +134,59 @@ __device__ inline void chunk_range(const BoundsParams &p, int c, int *t0, int *t
   *t1 = min(*t0 + p.chunk, (f + 1) * p.T);
 }
 
+// RMS normalisation of one token row held by `width` consecutive lanes, 8
+// elements each: x <- g * x / sqrt(mean(x^2) + eps).
+__device__ inline void rms_norm8(float *x, const float *g, int width, float inv_d, float eps) {
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+  ss = row_sum(ss, width);
+  const float r = 1.f / sqrtf(ss * inv_d + eps);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = g[e] * (x[e] * r);
+}
+
+// Rotary embedding of 4 dimension pairs (2i, 2i+1): each pair is rotated by
+// the angle whose cosine and sine are cs[i] and sn[i].
+__device__ inline void rope8(float *x, const float *cs, const float *sn) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = x[2 * i], b = x[2 * i + 1];
+    x[2 * i] = a * cs[i] - b * sn[i];
+    x[2 * i + 1] = a * sn[i] + b * cs[i];
+  }
+}
+
+// One token row of the input-producing chain: read Q, K and V, normalise and
+// rotate Q and K, write all three, and return Q and K as written (yq, yk).
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void bounds_pass1(BoundsParams p) {
+__device__ inline void produce_row(const BoundsParams &p, const ProduceParams &x, int b, int h, int64_t t,
+                                   int col, const float *gq, const float *gk, float *yq, float *yk) {
+  constexpr int TPR = D / 8;
+  const T *qi = static_cast<const T *>(x.qi) + b * x.qisb + h * x.qish + t * x.qisn + col * 8;
+  const T *ki = static_cast<const T *>(x.ki) + b * x.kisb + h * x.kish + t * x.kisn + col * 8;
+  const T *vi = static_cast<const T *>(x.vi) + b * x.visb + h * x.vish + t * x.visn + col * 8;
+  load8<T>(qi, yq);
+  load8<T>(ki, yk);
+  copy8<T>(vi, static_cast<T *>(x.vo) + b * x.vosb + h * x.vosh + t * x.vosn + col * 8);
+  if (x.gq) rms_norm8(yq, gq, TPR, 1.f / D, x.eps);
+  if (x.gk) rms_norm8(yk, gk, TPR, 1.f / D, x.eps);
+  if (x.rcos) {
+    const float4 c4 = *reinterpret_cast<const float4 *>(x.rcos + t * (D / 2) + col * 4);
+    const float4 s4 = *reinterpret_cast<const float4 *>(x.rsin + t * (D / 2) + col * 4);
+    const float cs[4] = {c4.x, c4.y, c4.z, c4.w}, sn[4] = {s4.x, s4.y, s4.z, s4.w};
+    rope8(yq, cs, sn);
+    rope8(yk, cs, sn);
+  }
+  store8<T>(const_cast<T *>(static_cast<const T *>(p.q)) + b * p.qsb + h * p.qsh + t * p.qsn + col * 8, yq);
+  store8<T>(const_cast<T *>(static_cast<const T *>(p.k)) + b * p.ksb + h * p.ksh + t * p.ksn + col * 8, yk);
+}
+
+// PRODUCE: the input-producing chain is fused in (fsattn_produce); the key
+// sums and query norms are then those of the values written, in the same
+// order, so they equal what pass 1 alone computes on the outputs.
+template <typename T, int D, bool PRODUCE>
+__global__ __launch_bounds__(kThreads) void bounds_pass1(BoundsParams p, ProduceParams xp) {
   constexpr int TPR = D / 8;            // threads per token row (8 elements each)
   constexpr int RPP = kThreads / TPR;   // rows per pass
   constexpr int U = 4;                  // passes whose loads are issued together
@@ -104,6 +200,14 @@ __global__ __launch_bounds__(kThreads) void bounds_pass1(BoundsParams p) {
   const T *k = static_cast<const T *>(p.k) + b * p.ksb + h * p.ksh + col * 8;
   int t0, t1;
   chunk_range(p, c, &t0, &t1);
+  [[maybe_unused]] float gq[8], gk[8];
+  if constexpr (PRODUCE) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      gq[e] = xp.gq ? xp.gq[h * D + col * 8 + e] : 1.f;
+      gk[e] = xp.gk ? xp.gk[h * D + col * 8 + e] : 1.f;
+    }
+  }
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float qm = 0.f;
   for (int t = t0 + r; t < t1; t += U * RPP) {
@@ -111,8 +215,12 @@ __global__ __launch_bounds__(kThreads) void bounds_pass1(BoundsParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (t + u * RPP < t1) {
-        load8<T>(k + (int64_t)(t + u * RPP) * p.ksn, x[u]);
-        load8<T>(q + (int64_t)(t + u * RPP) * p.qsn, y[u]);
+        if constexpr (PRODUCE) {
+          produce_row<T, D>(p, xp, b, h, t + u * RPP, col, gq, gk, y[u], x[u]);
+        } else {
+          load8<T>(k + (int64_t)(t + u * RPP) * p.ksn, x[u]);
+          load8<T>(q + (int64_t)(t + u * RPP) * p.qsn, y[u]);
+        }
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[u][e] = y[u][e] = 0.f;
@@ -275,11 +383,11 @@ __global__ __launch_bounds__(kThreads) void bounds_final(BoundsParams p) {
   }
 }
 
-template <typename T, int D>
-hipError_t launch_all(const BoundsParams &p, hipStream_t st) {
+template <typename T, int D, bool PRODUCE = false>
+hipError_t launch_all(const BoundsParams &p, hipStream_t st, const ProduceParams &x = ProduceParams{}) {
   const int BH = p.B * p.H;
   const int NC = p.F * p.chunks_per_frame;
-  hipLaunchKernelGGL((bounds_pass1<T, D>), dim3(NC, BH), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL((bounds_pass1<T, D, PRODUCE>), dim3(NC, BH), dim3(kThreads), 0, st, p, x);
   hipLaunchKernelGGL((bounds_head<D>), dim3(BH), dim3(kHeadThreads), 0, st, p);
   hipLaunchKernelGGL((bounds_pass2<T, D>), dim3(NC, BH), dim3(kThreads), 0, st, p);
   hipLaunchKernelGGL(bounds_final, dim3(BH), dim3(kThreads), 0, st, p);
@@ -295,6 +403,15 @@ hipError_t launch_head_bounds(const BoundsParams &p, int dtype, hipStream_t st) 
   }
   if (p.D == 128) return launch_all<float, 128>(p, st);
   return launch_all<float, 64>(p, st);
+}
+
+hipError_t launch_produce(const BoundsParams &p, const ProduceParams &x, int dtype, hipStream_t st) {
+  if (dtype == FSATTN_BF16) {
+    if (p.D == 128) return launch_all<__hip_bfloat16, 128, true>(p, st, x);
+    return launch_all<__hip_bfloat16, 64, true>(p, st, x);
+  }
+  if (p.D == 128) return launch_all<float, 128, true>(p, st, x);
+  return launch_all<float, 64, true>(p, st, x);
 }
 
 }  // namespace fsattn

@@ -60,6 +60,27 @@ WsLayout ws_layout(const fsattn_shape *s, const fsattn_mask *m) {
   return w;
 }
 
+BoundsParams bounds_params(const fsattn_shape *s, const fsattn_mask *m, const fsattn_tensor &q,
+                           const fsattn_tensor &k, float scale, float gap_threshold_nats, float *key_mean,
+                           fsattn_head_bound *rec, void *workspace, const WsLayout &w) {
+  BoundsParams p;
+  p.q = q.data; p.k = k.data;
+  p.qsb = q.stride_b; p.qsh = q.stride_h; p.qsn = q.stride_n;
+  p.ksb = k.stride_b; p.ksh = k.stride_h; p.ksn = k.stride_n;
+  p.B = s->batch; p.H = s->heads; p.N = s->seq_len; p.F = m->num_frames; p.T = m->tokens_per_frame;
+  p.D = s->head_dim;
+  p.live = live_geom(*m);
+  p.chunk = kBoundsChunk; p.chunks_per_frame = w.chunks_per_frame;
+  p.scale = scale; p.threshold = gap_threshold_nats;
+  p.key_mean = key_mean; p.rec = rec;
+  char *base = static_cast<char *>(workspace);
+  p.ws_part = reinterpret_cast<float *>(base + w.part);
+  p.ws_frame = reinterpret_cast<float *>(base + w.frame);
+  p.ws_qmax = reinterpret_cast<float *>(base + w.qmax);
+  p.ws_kmax = reinterpret_cast<float *>(base + w.kmax);
+  return p;
+}
+
 }  // namespace
 
 extern "C" int fsattn_abi_version(void) { return FSATTN_ABI_VERSION; }
@@ -109,22 +130,42 @@ extern "C" fsattn_status fsattn_head_bounds(void *hip_stream, const fsattn_shape
   if (!key_mean || !rec || !workspace) return FSATTN_ERR_INVALID_ARGUMENT;
   const WsLayout w = ws_layout(s, m);
   if (workspace_bytes < w.total) return FSATTN_ERR_BUFFER_TOO_SMALL;
-  BoundsParams p;
-  p.q = q.data; p.k = k.data;
-  p.qsb = q.stride_b; p.qsh = q.stride_h; p.qsn = q.stride_n;
-  p.ksb = k.stride_b; p.ksh = k.stride_h; p.ksn = k.stride_n;
-  p.B = s->batch; p.H = s->heads; p.N = s->seq_len; p.F = m->num_frames; p.T = m->tokens_per_frame;
-  p.D = s->head_dim;
-  p.live = live_geom(*m);
-  p.chunk = kBoundsChunk; p.chunks_per_frame = w.chunks_per_frame;
-  p.scale = scale; p.threshold = gap_threshold_nats;
-  p.key_mean = key_mean; p.rec = rec;
-  char *base = static_cast<char *>(workspace);
-  p.ws_part = reinterpret_cast<float *>(base + w.part);
-  p.ws_frame = reinterpret_cast<float *>(base + w.frame);
-  p.ws_qmax = reinterpret_cast<float *>(base + w.qmax);
-  p.ws_kmax = reinterpret_cast<float *>(base + w.kmax);
+  const BoundsParams p = bounds_params(s, m, q, k, scale, gap_threshold_nats, key_mean, rec, workspace, w);
   const hipError_t e = launch_head_bounds(p, s->dtype, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? FSATTN_OK : FSATTN_ERR_HIP;
+}
+
+extern "C" fsattn_status fsattn_produce(void *hip_stream, const fsattn_shape *s, const fsattn_mask *m,
+                                        fsattn_tensor q_in, fsattn_tensor k_in, fsattn_tensor v_in,
+                                        const float *gamma_q, const float *gamma_k, float eps,
+                                        const float *rope_cos, const float *rope_sin, fsattn_tensor q,
+                                        fsattn_tensor k, fsattn_tensor v, float scale,
+                                        float gap_threshold_nats, float *key_mean, fsattn_head_bound *rec,
+                                        void *workspace, size_t workspace_bytes) {
+  fsattn_status st = check_shape(s, m);
+  if (st != FSATTN_OK) return st;
+  const int esz = elem_size(s->dtype);
+  for (const fsattn_tensor *t : {&q_in, &k_in, &v_in, &q, &k, &v})
+    if ((st = check_tensor(*t, esz, s->head_dim)) != FSATTN_OK) return st;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return FSATTN_ERR_INVALID_ARGUMENT;
+  if (!(gap_threshold_nats >= 0.f)) return FSATTN_ERR_INVALID_ARGUMENT;
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return FSATTN_ERR_INVALID_ARGUMENT;
+  if (!key_mean || !rec || !workspace) return FSATTN_ERR_INVALID_ARGUMENT;
+  if ((rope_cos == nullptr) != (rope_sin == nullptr)) return FSATTN_ERR_INVALID_ARGUMENT;
+  for (const float *g : {gamma_q, gamma_k, rope_cos, rope_sin})
+    if (reinterpret_cast<uintptr_t>(g) % 16) return FSATTN_ERR_INVALID_ARGUMENT;
+  const WsLayout w = ws_layout(s, m);
+  if (workspace_bytes < w.total) return FSATTN_ERR_BUFFER_TOO_SMALL;
+  const BoundsParams p = bounds_params(s, m, q, k, scale, gap_threshold_nats, key_mean, rec, workspace, w);
+  ProduceParams x;
+  x.qi = q_in.data; x.ki = k_in.data; x.vi = v_in.data;
+  x.qisb = q_in.stride_b; x.qish = q_in.stride_h; x.qisn = q_in.stride_n;
+  x.kisb = k_in.stride_b; x.kish = k_in.stride_h; x.kisn = k_in.stride_n;
+  x.visb = v_in.stride_b; x.vish = v_in.stride_h; x.visn = v_in.stride_n;
+  x.vo = v.data; x.vosb = v.stride_b; x.vosh = v.stride_h; x.vosn = v.stride_n;
+  x.gq = gamma_q; x.gk = gamma_k; x.rcos = rope_cos; x.rsin = rope_sin;
+  x.eps = eps;
+  const hipError_t e = launch_produce(p, x, s->dtype, static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? FSATTN_OK : FSATTN_ERR_HIP;
 }
 

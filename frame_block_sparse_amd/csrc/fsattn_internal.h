@@ -83,6 +83,22 @@ struct BoundsParams {
 
 hipError_t launch_head_bounds(const BoundsParams &p, int dtype, hipStream_t st);
 
+// The input-producing chain fused into the bounds' first pass
+// (fsattn_produce): Q, K and V are read through the input views, Q and K are
+// RMS-normalised (gamma [H][d], when given) and rotated (angle tables
+// [N][d/2], when given), and all three are written through the output
+// views, which are BoundsParams' q and k (and vo here for V).
+struct ProduceParams {
+  const void *qi, *ki, *vi;
+  int64_t qisb, qish, qisn, kisb, kish, kisn, visb, vish, visn;
+  void *vo;
+  int64_t vosb, vosh, vosn;
+  const float *gq, *gk;         // [H][d] or null (no normalisation)
+  const float *rcos, *rsin;     // [N][d/2] or null (no rotation)
+  float eps;
+};
+hipError_t launch_produce(const BoundsParams &p, const ProduceParams &x, int dtype, hipStream_t st);
+
 // Device plan (same arrays as fsattn_plan); the mask is already validated.
 hipError_t launch_plan_device(const fsattn_mask &m, int32_t *row_ptr, int32_t *col_idx, hipStream_t st);
 

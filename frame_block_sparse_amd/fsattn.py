@@ -82,6 +82,10 @@ def lib() -> ctypes.CDLL:
     L.fsattn_head_bounds.argtypes = [ctypes.c_void_p, ctypes.POINTER(Shape), ctypes.POINTER(Mask), Tensor, Tensor,
                                      ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_size_t]
+    L.fsattn_produce.argtypes = [ctypes.c_void_p, ctypes.POINTER(Shape), ctypes.POINTER(Mask), Tensor, Tensor,
+                                 Tensor, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
+                                 ctypes.c_void_p, Tensor, Tensor, Tensor, ctypes.c_float, ctypes.c_float,
+                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]
     L.fsattn_forward.argtypes = [ctypes.c_void_p, ctypes.POINTER(Shape), ctypes.POINTER(Mask),
                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                  Tensor, Tensor, Tensor, Tensor, ctypes.c_int32, ctypes.c_void_p,
@@ -100,7 +104,8 @@ def lib() -> ctypes.CDLL:
     if L.fsattn_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{LIB_PATH} has ABI {L.fsattn_abi_version()}, the binding expects {ABI_VERSION}: "
                            "rebuild it")
-    for name in ("fsattn_plan_size", "fsattn_plan", "fsattn_plan_device", "fsattn_head_bounds", "fsattn_forward",
+    for name in ("fsattn_plan_size", "fsattn_plan", "fsattn_plan_device", "fsattn_head_bounds", "fsattn_produce",
+                 "fsattn_forward",
                  "fsattn_forward_launch_info", "fsattn_mfma_probe", "fsattn_prior_art_forward"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -265,6 +270,49 @@ def head_bounds(q: torch.Tensor, k: torch.Tensor, mask, scale: Optional[float] =
                                 float(scale), float(threshold), out.key_mean.data_ptr(), out.rec.data_ptr(),
                                 workspace.data_ptr(), workspace.numel()), "fsattn_head_bounds")
     return out
+
+
+def _f32_ptr(t: Optional[torch.Tensor], shape, what: str) -> int:
+    if t is None:
+        return 0
+    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise FsattnError(1, f"{what} must be a contiguous float32 tensor of shape {tuple(shape)}")
+    return t.data_ptr()
+
+
+def produce(q_in: torch.Tensor, k_in: torch.Tensor, v_in: torch.Tensor, mask,
+            gamma_q: Optional[torch.Tensor] = None, gamma_k: Optional[torch.Tensor] = None, eps: float = 1e-6,
+            rope_cos: Optional[torch.Tensor] = None, rope_sin: Optional[torch.Tensor] = None,
+            out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None, scale: Optional[float] = None,
+            threshold: float = DEFAULT_GAP_NATS, workspace: Optional[torch.Tensor] = None,
+            bounds: Optional[Bounds] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, Bounds]:
+    """fsattn_produce: Q, K (RMS-normalised with gamma [H, d], then rotated
+    with the angle tables [N, d/2]) and V written through `out` (default:
+    new contiguous [B, H, N, d] tensors), plus the bound records of the
+    values written. Inputs may be any [B, H, N, d] views with a contiguous
+    last axis, e.g. slices of a token-major QKV projection output."""
+    m = to_mask(mask)
+    s = _shape(q_in)
+    B, H, N, d = q_in.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    L = lib()
+    if out is None:
+        out = tuple(torch.empty((B, H, N, d), dtype=q_in.dtype, device=q_in.device) for _ in range(3))
+    need = L.fsattn_head_bounds_workspace_bytes(ctypes.byref(s), ctypes.byref(m))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_in.device)
+    if bounds is None:
+        bounds = Bounds(torch.empty((B, H, d), dtype=torch.float32, device=q_in.device),
+                        torch.empty((B, H, 8), dtype=torch.float32, device=q_in.device))
+    q, k, v = out
+    _check(L.fsattn_produce(_stream(q_in), ctypes.byref(s), ctypes.byref(m), _tensor(q_in), _tensor(k_in),
+                            _tensor(v_in), _f32_ptr(gamma_q, (H, d), "gamma_q"), _f32_ptr(gamma_k, (H, d), "gamma_k"),
+                            float(eps), _f32_ptr(rope_cos, (N, d // 2), "rope_cos"),
+                            _f32_ptr(rope_sin, (N, d // 2), "rope_sin"), _tensor(q), _tensor(k), _tensor(v),
+                            float(scale), float(threshold), bounds.key_mean.data_ptr(), bounds.rec.data_ptr(),
+                            workspace.data_ptr(), workspace.numel()), "fsattn_produce")
+    return q, k, v, bounds
 
 
 # ----------------------------------------------------------------- forward

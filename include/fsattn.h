@@ -7,6 +7,8 @@
  *   fsattn_head_bounds  key mean, norm maxima, logit bound, eligibility (GPU)
  *   fsattn_forward      attention over the live blocks, fixed-shift or
  *                       online softmax chosen per head (GPU)
+ * and fsattn_produce, the chain that makes Q, K and V (normalisation and
+ * rotary embedding) fused with fsattn_head_bounds (GPU).
  *
  * The method is the one described in "HeyGen x Google Cloud: Bringing
  * Avatar IV to TPUs" (Google Developers Blog). Section names below refer to
@@ -210,6 +212,39 @@ fsattn_status fsattn_head_bounds(void *hip_stream, const fsattn_shape *s, const 
                                  fsattn_tensor q, fsattn_tensor k, float scale,
                                  float gap_threshold_nats, float *key_mean,
                                  fsattn_head_bound *rec, void *workspace, size_t workspace_bytes);
+
+/*
+ * The input-producing chain fused with the bounds ("Layout Is the ABI",
+ * Fig. 5: the small operations that make attention's inputs run as one
+ * kernel that writes its consumer's layout). Reads Q, K and V through the
+ * views q_in, k_in, v_in (any [B,H,N,d] strides, e.g. the token-major
+ * output of a QKV projection: stride_n = 3*H*d, stride_h = d); for Q and K
+ * applies, per token row and in this order,
+ *   RMS normalisation  x <- gamma[h] * x / sqrt(mean(x^2) + eps)
+ *   rotary embedding   pair (x[2i], x[2i+1]) of token n rotated by the angle
+ *                      with cosine rope_cos[n*d/2 + i], sine rope_sin[...]
+ * and writes Q, K and the unchanged V, rounded to s->dtype, through the
+ * views q, k, v. gamma_q / gamma_k: device fp32 [H][d], 16-byte aligned,
+ * or NULL (that operand is not normalised); eps >= 0. rope_cos / rope_sin:
+ * device fp32 [N][d/2], 16-byte aligned, both or neither (NULL: no
+ * rotation); the tables carry the positional scheme (1-D or per-axis video
+ * positions alike). Inputs and outputs have s->dtype. An output may be the
+ * same view as its input (in place); other overlaps are undefined.
+ * In the same pass it accumulates the statistics of fsattn_head_bounds on
+ * the values it writes, then finishes the bounds: key_mean, rec, scale,
+ * gap_threshold_nats and workspace (>= fsattn_head_bounds_workspace_bytes)
+ * are as there, and the results equal, bit for bit, fsattn_head_bounds
+ * called on the outputs. Asynchronous on hip_stream.
+ * Errors: INVALID_ARGUMENT, BLOCK_GEOMETRY, UNSUPPORTED, BUFFER_TOO_SMALL,
+ * HIP.
+ */
+fsattn_status fsattn_produce(void *hip_stream, const fsattn_shape *s, const fsattn_mask *m,
+                             fsattn_tensor q_in, fsattn_tensor k_in, fsattn_tensor v_in,
+                             const float *gamma_q, const float *gamma_k, float eps,
+                             const float *rope_cos, const float *rope_sin,
+                             fsattn_tensor q, fsattn_tensor k, fsattn_tensor v, float scale,
+                             float gap_threshold_nats, float *key_mean, fsattn_head_bound *rec,
+                             void *workspace, size_t workspace_bytes);
 
 /*
  * Attention over the live blocks:

@@ -235,3 +235,28 @@ def test_prior_art_forward_validates_on_host():
         mg = F.to_mask(t)
         assert L.fsattn_prior_art_forward(None, ctypes.byref(s), ctypes.byref(mg), _t(), _t(), _t(), _t(), 1,
                                           0.125, FAKE, need) == 3
+
+
+def test_produce_validates_on_host():
+    L = fs.lib()
+    s = F.Shape(1, 2, 240, 64, 1)
+    m = F.to_mask((5, 48, 1, 1, 0, 16, 16))
+    need = L.fsattn_head_bounds_workspace_bytes(ctypes.byref(s), ctypes.byref(m))
+
+    def call(shape=s, gq=FAKE, gk=FAKE, eps=1e-6, cs=FAKE, sn=FAKE, km=FAKE, ws=FAKE, wsb=need, qin=None,
+             scale=0.125, mask=m):
+        return L.fsattn_produce(None, ctypes.byref(shape), ctypes.byref(mask), qin or _t(), _t(), _t(), gq, gk, eps,
+                                cs, sn, _t(), _t(), _t(), scale, 30.0, km, FAKE, ws, wsb)
+    assert call(gq=FAKE + 4) == 1                  # misaligned gamma
+    assert call(cs=None) == 1                      # one table without the other
+    assert call(sn=None) == 1
+    assert call(eps=-1.0) == 1
+    assert call(eps=float("inf")) == 1
+    assert call(km=None) == 1
+    assert call(ws=None) == 1
+    assert call(wsb=need - 1) == 4
+    assert call(scale=0.0) == 1
+    assert call(qin=F.Tensor(FAKE, 0, 0, 32)) == 1                     # stride_n < head_dim
+    assert call(shape=F.Shape(1, 2, 240, 96, 1)) == 3                   # head_dim not built
+    assert call(shape=F.Shape(1, 2, 241, 64, 1)) == 1                   # seq_len != F*T
+    assert call(mask=F.to_mask((5, 48, 1, 1, 0, 32, 16))) == 2

@@ -473,3 +473,102 @@ def test_prior_art_comparator_on_workloads(dev, config_inputs, i):
     ref, _ = oracle.attention_ref(q, k, v, _geom(w), rows=rows)
     assert np.abs(out.float().cpu().numpy()[:, :, rows] - ref).max() <= TOL["bf16"]
     assert (out.float() - mine.float()).abs().max().item() <= TOL["bf16"]
+
+
+# ------------------------------------------------------------------ producer (norm + rotary + layout)
+
+def _packed_views(arrs, dtype, dev):
+    """q, k, v (B, H, N, d) packed token-major as one [B, N, 3, H, d] tensor
+    (a QKV projection's output) and the three [B, H, N, d] views into it."""
+    qkv = torch.from_numpy(np.ascontiguousarray(np.stack(arrs, axis=2).transpose(0, 3, 2, 1, 4)))
+    qkv = qkv.to(dtype).to(dev)
+    return qkv, [qkv[:, :, i].permute(0, 2, 1, 3) for i in range(3)]
+
+
+def _produce_tol(dt, ref):
+    # bf16: one ulp of the output (2^-7 relative) covers the rounding of an
+    # fp32 result that may sit next to a rounding boundary; fp32: 1e-5
+    return 2.0 ** -7 * np.abs(ref) + 1e-6 if dt == "bf16" else 1e-5
+
+
+PRODUCE_CASES = [
+    # (name, B, H, F, T, d, dtype, norm, rope, in_place)
+    ("bf16_d128", 1, 3, 4, 96, 128, "bf16", True, True, False),
+    ("bf16_d64_two_batches", 2, 2, 3, 80, 64, "bf16", True, True, False),
+    ("bf16_norm_only", 1, 2, 3, 64, 128, "bf16", True, False, False),
+    ("bf16_rope_only", 1, 2, 3, 64, 128, "bf16", False, True, False),
+    ("bf16_copy_only", 1, 2, 3, 48, 64, "bf16", False, False, False),
+    ("bf16_in_place", 1, 2, 5, 48, 128, "bf16", True, True, True),
+    ("f32_d128", 1, 2, 3, 80, 128, "f32", True, True, False),
+    ("f32_d64_in_place", 2, 1, 4, 48, 64, "f32", True, True, True),
+]
+
+
+@pytest.mark.parametrize("case", PRODUCE_CASES, ids=[c[0] for c in PRODUCE_CASES])
+def test_produce_parity(dev, case):
+    name, B, H, F_, T, d, dt, norm, rope, in_place = case
+    _say(f"[produce] {name}")
+    w = workloads.make_workload(name, B, H, F_, T, d, dt, 1, 1, 0, 16, 16)
+    x = workloads.make_producer_inputs(w, seed=5)
+    cos, sin = oracle.rope_tables_1d(w.seq_len, d)
+    cos, sin = cos.astype(np.float32), sin.astype(np.float32)
+    td = _tdtype(w)
+    qkv, views = _packed_views((x["q"], x["k"], x["v"]), td, dev)
+    gq = torch.from_numpy(x["gamma_q"]).to(dev) if norm else None
+    gk = torch.from_numpy(x["gamma_k"]).to(dev) if norm else None
+    tc = torch.from_numpy(cos).to(dev) if rope else None
+    ts = torch.from_numpy(sin).to(dev) if rope else None
+    out = tuple(views) if in_place else None
+    q, k, v, bnd = fs.produce(*views, w, gq, gk, 1e-6, tc, ts, out=out)
+    torch.cuda.synchronize()
+    if in_place:
+        assert q.data_ptr() == views[0].data_ptr()
+    rq, rk, rv = oracle.produce_ref(x["q"], x["k"], x["v"], x["gamma_q"] if norm else None,
+                                    x["gamma_k"] if norm else None, 1e-6, cos if rope else None,
+                                    sin if rope else None)
+    for got, ref, nm in ((q, rq, "q"), (k, rk, "k")):
+        g = got.float().cpu().numpy()
+        assert np.all(np.abs(g - ref) <= _produce_tol(dt, ref)), (nm, np.abs(g - ref).max())
+    assert np.array_equal(v.float().cpu().numpy(), rv)             # V is copied unchanged
+    # the bound records are those of the values written
+    ref_b = fs.head_bounds(q, k, w)
+    torch.cuda.synchronize()
+    assert torch.equal(bnd.rec, ref_b.rec) and torch.equal(bnd.key_mean, ref_b.key_mean)
+
+
+def test_produce_then_forward_full_size(dev):
+    """6 frames x 8160 tokens, 4 heads, d = 128, bf16 (the RMS-normalised
+    workload's shape) from raw token-major projections: fsattn_produce
+    (RMSNorm + rotary embedding + layout + bounds), then the forward in the
+    library's default launch. Checked: Q, K, V against the oracle on every
+    element; the bound records bit for bit against fsattn_head_bounds on the
+    outputs and against the oracle; sampled output rows of every frame
+    against the oracle's attention on the produced Q, K, V."""
+    w = workloads.config(5)
+    _say(f"[produce] {w.name} full size, then forward")
+    x = workloads.make_producer_inputs(w, seed=6)
+    qkv, views = _packed_views((x["q"], x["k"], x["v"]), torch.bfloat16, dev)
+    args = [torch.from_numpy(x[n]).to(dev) for n in ("gamma_q", "gamma_k")]
+    tabs = [torch.from_numpy(x[n]).to(dev) for n in ("cos", "sin")]
+    q, k, v, bnd = fs.produce(*views, w, args[0], args[1], workloads.RMS_EPS, tabs[0], tabs[1])
+    dp = fs.device_plan(w, dev)
+    o = fs.forward(q, k, v, dp, bnd)
+    ref_b = fs.head_bounds(q, k, w)
+    torch.cuda.synchronize()
+    assert torch.equal(bnd.rec, ref_b.rec) and torch.equal(bnd.key_mean, ref_b.key_mean)
+    rq, rk, rv = oracle.produce_ref(x["q"], x["k"], x["v"], x["gamma_q"], x["gamma_k"], workloads.RMS_EPS,
+                                    x["cos"], x["sin"])
+    qn, kn, vn = (t.float().cpu().numpy() for t in (q, k, v))
+    for g, ref, nm in ((qn, rq, "q"), (kn, rk, "k")):
+        assert np.all(np.abs(g - ref) <= _produce_tol("bf16", ref)), (nm, np.abs(g - ref).max())
+    assert np.array_equal(vn, rv)
+    g = _geom(w)
+    rec = oracle.head_bounds_ref(qn, kn, g)
+    got = bnd.host()
+    np.testing.assert_allclose(got["bound"], rec["bound"], rtol=1e-5)
+    assert np.array_equal(got["eligible"].astype(bool), rec["eligible"])
+    rows = _sample_rows(w, per_frame=24, seed=7)
+    ref_o, _ = oracle.attention_ref(qn, kn, vn, g, rows=rows)
+    err = np.abs(o.float().cpu().numpy()[:, :, rows] - ref_o).max()
+    _say(f"    max abs err {err:.3e}")
+    assert err <= TOL["bf16"], err

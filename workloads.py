@@ -149,3 +149,24 @@ def make_inputs(w: Workload, seed: int = 0, rows: Optional[int] = None):
     elif w.dtype != "f32":
         raise ValueError(w.dtype)
     return q, k, v
+
+
+def make_producer_inputs(w: Workload, seed: int = 0):
+    """Inputs of the input-producing chain (normalisation + rotary embedding)
+    at the workload's shape: raw projections q, k, v ~ N(0, 1) as float32
+    (B, H, N, d), bf16-representable for bf16 workloads; per-head gammas
+    (H, d) ~ U(0.5, 1.5); and rotation tables (N, d/2) as float32 cosines and
+    sines of angles ~ U(0, 2 pi). Drawn in that order from one seeded
+    generator."""
+    rng = np.random.default_rng(seed)
+    shape = (w.batch, w.heads, w.seq_len, w.head_dim)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    gq = rng.uniform(0.5, 1.5, (w.heads, w.head_dim)).astype(np.float32)
+    gk = rng.uniform(0.5, 1.5, (w.heads, w.head_dim)).astype(np.float32)
+    ang = rng.uniform(0.0, 2.0 * np.pi, (w.seq_len, w.head_dim // 2))
+    if w.dtype == "bf16":
+        q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
+    return dict(q=q, k=k, v=v, gamma_q=gq, gamma_k=gk,
+                cos=np.cos(ang).astype(np.float32), sin=np.sin(ang).astype(np.float32))
