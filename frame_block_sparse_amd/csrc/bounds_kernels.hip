@@ -178,8 +178,8 @@ __device__ inline void produce_row(const BoundsParams &p, const ProduceParams &x
     rope8(yq, cs, sn);
     rope8(yk, cs, sn);
   }
-  store8<T>(const_cast<T *>(static_cast<const T *>(p.q)) + b * p.qsb + h * p.qsh + t * p.qsn + col * 8, yq);
-  store8<T>(const_cast<T *>(static_cast<const T *>(p.k)) + b * p.ksb + h * p.ksh + t * p.ksn + col * 8, yk);
+  store8<T>(static_cast<T *>(x.qo) + b * p.qsb + h * p.qsh + t * p.qsn + col * 8, yq);
+  store8<T>(static_cast<T *>(x.ko) + b * p.ksb + h * p.ksh + t * p.ksn + col * 8, yk);
 }
 
 // PRODUCE: the input-producing chain is fused in (fsattn_produce); the key

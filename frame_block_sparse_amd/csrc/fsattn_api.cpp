@@ -162,6 +162,7 @@ extern "C" fsattn_status fsattn_produce(void *hip_stream, const fsattn_shape *s,
   x.qisb = q_in.stride_b; x.qish = q_in.stride_h; x.qisn = q_in.stride_n;
   x.kisb = k_in.stride_b; x.kish = k_in.stride_h; x.kisn = k_in.stride_n;
   x.visb = v_in.stride_b; x.vish = v_in.stride_h; x.visn = v_in.stride_n;
+  x.qo = q.data; x.ko = k.data;   // read back by the bounds through p.q, p.k (same strides)
   x.vo = v.data; x.vosb = v.stride_b; x.vosh = v.stride_h; x.vosn = v.stride_n;
   x.gq = gamma_q; x.gk = gamma_k; x.rcos = rope_cos; x.rsin = rope_sin;
   x.eps = eps;

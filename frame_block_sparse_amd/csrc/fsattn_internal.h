@@ -87,11 +87,12 @@ hipError_t launch_head_bounds(const BoundsParams &p, int dtype, hipStream_t st);
 // (fsattn_produce): Q, K and V are read through the input views, Q and K are
 // RMS-normalised (gamma [H][d], when given) and rotated (angle tables
 // [N][d/2], when given), and all three are written through the output
-// views, which are BoundsParams' q and k (and vo here for V).
+// views qo, ko, vo; qo and ko are the views BoundsParams' q and k then read
+// (same pointers and strides).
 struct ProduceParams {
   const void *qi, *ki, *vi;
   int64_t qisb, qish, qisn, kisb, kish, kisn, visb, vish, visn;
-  void *vo;
+  void *qo, *ko, *vo;
   int64_t vosb, vosh, vosn;
   const float *gq, *gk;         // [H][d] or null (no normalisation)
   const float *rcos, *rsin;     // [N][d/2] or null (no rotation)
