@@ -572,3 +572,61 @@ def test_produce_then_forward_full_size(dev):
     err = np.abs(o.float().cpu().numpy()[:, :, rows] - ref_o).max()
     _say(f"    max abs err {err:.3e}")
     assert err <= TOL["bf16"], err
+
+
+# ------------------------------------------------------------------ degenerate inputs
+
+DEGENERATE = ["q_zero", "keys_equal", "v_constant", "wide_logits"]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("kind", DEGENERATE)
+def test_forward_degenerate_inputs(dev, kind, dt):
+    """Degenerate cases of the method, in the library's default launch:
+    Q = 0 (every logit 0: the bound, gap and shift are 0 and each row is the
+    mean of its live V rows); all keys equal (K_max = C_max = 0: the shift is
+    exact); V constant (every row is that constant); and logits with a spread
+    of tens of nats (the heads fail eligibility and take the online path)."""
+    _say(f"[fwd-degenerate] {kind} {dt}")
+    w = workloads.make_workload(f"deg_{kind}", 1, 2, 4, 96, 128 if dt == "bf16" else 64, dt, 1, 1, 0, 48, 32)
+    q, k, v = workloads.make_inputs(w, seed=8)
+    if kind == "q_zero":
+        q = np.zeros_like(q)
+    elif kind == "keys_equal":
+        k = np.broadcast_to(k[:, :, :1, :], k.shape).copy()
+    elif kind == "v_constant":
+        v = np.broadcast_to(v[:, :, :1, :], v.shape).copy()
+    elif kind == "wide_logits":
+        q, k = q * np.float32(3.0), k * np.float32(3.0)
+        if dt == "bf16":
+            q, k = workloads.round_to_bf16(q), workloads.round_to_bf16(k)
+    out, bnd, lse = _run(w, q, k, v, dev, lse=True)
+    o = out.float().cpu().numpy()
+    rec = bnd.host()
+    g = _geom(w)
+    ref, ref_lse = oracle.attention_ref(q, k, v, g)
+    assert np.isfinite(o).all() and np.isfinite(lse.cpu().numpy()).all()
+    assert np.abs(o - ref).max() <= TOL[dt], np.abs(o - ref).max()
+    # Log-sum-exp bound: LSE_TOL covers the rounding of the weights; with
+    # logits of tens of nats the fp32 rounding of the logits themselves also
+    # counts: a d-term fp32 dot product is off by at most d * 2^-24 times
+    # scale * sum |q_t k_t| <= scale * |q| |k|, so the bound adds that term
+    # (negligible for the other inputs here).
+    qn = np.linalg.norm(q.astype(np.float64), axis=-1).max()
+    kn = np.linalg.norm(k.astype(np.float64), axis=-1).max()
+    lse_tol = LSE_TOL[dt] + w.head_dim * 2.0 ** -24 * qn * kn / math.sqrt(w.head_dim)
+    assert np.abs(lse.cpu().numpy() - ref_lse).max() <= lse_tol
+    if kind == "q_zero":
+        assert np.all(rec["bound"] == 0) and np.all(rec["gap_est"] == 0) and rec["eligible"].all()
+        M = oracle.token_mask(g)
+        mean_v = (M.astype(np.float64) @ v[0, 0].astype(np.float64)) / M.sum(axis=1, keepdims=True)
+        assert np.abs(o[0, 0] - mean_v).max() <= TOL[dt]
+    elif kind == "keys_equal":
+        # (exactly 0 for bf16 keys: the sums of equal bf16 values are exact in fp32)
+        kn = float(np.linalg.norm(k[0, 0, 0]))
+        assert np.all(rec["k_norm_max"] <= 1e-6 * kn) and np.all(rec["c_max"] <= 1e-6 * kn)
+        assert rec["eligible"].all()
+    elif kind == "v_constant":
+        assert np.abs(o - v[:, :, :1, :]).max() <= (2.0 ** -8 if dt == "bf16" else 2e-6) * np.abs(v).max()
+    elif kind == "wide_logits":
+        assert not rec["eligible"].any(), rec["gap_est"]
