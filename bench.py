@@ -70,10 +70,14 @@ def partial_tile_share(w, tile: int = 128):
     import numpy as np
     F_, T, N = w.num_frames, w.tokens_per_frame, w.seq_len
     live = np.zeros((F_, F_), dtype=np.int64)   # live[f, g]: key frame g is visible from query frame f
+    r = w.ref_frame
+    nr = max(1, w.ref_count) if r >= 0 else 0     # reference frames r .. r + nr - 1
     for f in range(F_):
         live[f, max(0, f - w.window_before):min(F_ - 1, f + w.window_after) + 1] = 1
-        if w.ref_frame >= 0:
-            live[f, w.ref_frame] = 1
+        if nr:
+            live[f, r:r + nr] = 1
+    if nr and w.ref_queries_global:
+        live[r:r + nr, :] = 1
     pre = np.zeros((F_ + 1, F_ + 1), dtype=np.int64)
     pre[1:, 1:] = live.cumsum(0).cumsum(1)
     nt = -(-N // tile)
