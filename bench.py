@@ -139,6 +139,42 @@ def prior_art_timing(w, qd, kd, vd, fwd_ms: float, live_flops: float, reps: int 
                     "per-element frame predicates on partly live tiles, online softmax, fp32 (O, lse) merge"}
 
 
+def mask_variant_timing(w, qd, kd, vd, reps: int = 10):
+    """The forward (library default launch) on the same inputs under the mask
+    variants: a global reference frame (its queries see every frame), a span
+    of 2 reference frames, and a global span of 3. Live FLOPs / average
+    launch time from HIP events, against the bf16 peak."""
+    import dataclasses
+    import torch
+    import frame_block_sparse_amd as fs
+    from frame_block_sparse_amd import fsattn as F
+    out = []
+    for rg, nr in ((1, 0), (0, 2), (1, 3)):
+        if w.ref_frame < 0 or w.ref_frame + max(1, nr) > w.num_frames:
+            continue
+        wv = dataclasses.replace(w, ref_queries_global=rg, ref_count=nr)
+        m = F.to_mask(wv)
+        _, nnz = fs.plan_size(m)
+        flops = 4.0 * w.head_dim * w.batch * w.heads * nnz * w.block_q * w.block_k
+        dp = fs.plan_on_device(m, qd.device)
+        bnd = fs.head_bounds(qd, kd, m)
+        o = torch.empty_like(qd)
+        for _ in range(3):
+            fs.forward(qd, kd, vd, dp, bnd, out=o)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            fs.forward(qd, kd, vd, dp, bnd, out=o)
+            b.record()
+        torch.cuda.synchronize()
+        avg = sum(a.elapsed_time(b) for a, b in ev) / reps
+        tf = flops / (avg * 1e-3) / 1e12
+        out.append({"ref_queries_global": rg, "ref_count": nr, "live_gflop": round(flops / 1e9, 2),
+                    "avg_ms": round(avg, 5), "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                    "eligible_heads": int(bnd.host()["eligible"].sum())})
+    return out
+
+
 def producer_timing(w, dev, bounds_ms: float, reps: int = 20):
     """fsattn_produce at the workload's shape, from a token-major packed
     projection output [B, N, 3, H, d]: RMSNorm(gamma) and rotary embedding of
@@ -336,6 +372,7 @@ def main():
     prior = prior_art_timing(w, qd, kd, vd, fwd_avg, live_flops) if w.dtype == "bf16" else None
     value = live_flops / (ms_step * 1e-3) / 1e12
     producer = producer_timing(w, dev, bnd_avg)
+    variants = mask_variant_timing(w, qd, kd, vd) if w.dtype == "bf16" else None
     elig = bnd.host()["eligible"]
     esz = 2 if w.dtype == "bf16" else 4
     bounds_bytes = 2.0 * w.batch * w.heads * w.seq_len * w.head_dim * esz
@@ -378,6 +415,7 @@ def main():
         "bounds": {"avg_ms": round(bnd_avg, 5), "algorithmic_bytes": bounds_bytes,
                    "GBps": round(bounds_bytes / (bnd_avg * 1e-3) / 1e9, 1), "peak_GBps": PEAK_HBM_GBS},
         "producer": producer,
+        "mask_variants": variants,
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle, bounded sample)", file=sys.stderr, flush=True)
