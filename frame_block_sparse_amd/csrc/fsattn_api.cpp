@@ -14,7 +14,11 @@ using namespace fsattn;
 
 namespace {
 
-constexpr int kBoundsChunk = 128;   // tokens per bounds-kernel workgroup (within one frame)
+// Tokens per bounds-kernel workgroup (within one frame): 128, or 256 for
+// frames of 4096 tokens or more, where halving the chunk partial sums that
+// the per-head kernel adds up outweighs the fewer workgroups (measured on
+// 8160-token frames: 8 % less time; equal at 3600, slower at 960).
+int bounds_chunk(int tokens_per_frame) { return tokens_per_frame >= 4096 ? 256 : 128; }
 
 int elem_size(int dtype) { return dtype == FSATTN_BF16 ? 2 : 4; }
 
@@ -40,7 +44,7 @@ fsattn_status check_tensor(const fsattn_tensor &t, int esz, int head_dim) {
 
 struct WsLayout {
   size_t part, frame, qmax, kmax, total;
-  int chunks_per_frame;
+  int chunk, chunks_per_frame;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -48,7 +52,8 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 WsLayout ws_layout(const fsattn_shape *s, const fsattn_mask *m) {
   WsLayout w;
   const int64_t BH = (int64_t)s->batch * s->heads;
-  w.chunks_per_frame = (m->tokens_per_frame + kBoundsChunk - 1) / kBoundsChunk;
+  w.chunk = bounds_chunk(m->tokens_per_frame);
+  w.chunks_per_frame = (m->tokens_per_frame + w.chunk - 1) / w.chunk;
   const int64_t NC = (int64_t)m->num_frames * w.chunks_per_frame;
   const int64_t D = s->head_dim;
   size_t off = 0;
@@ -70,7 +75,7 @@ BoundsParams bounds_params(const fsattn_shape *s, const fsattn_mask *m, const fs
   p.B = s->batch; p.H = s->heads; p.N = s->seq_len; p.F = m->num_frames; p.T = m->tokens_per_frame;
   p.D = s->head_dim;
   p.live = live_geom(*m);
-  p.chunk = kBoundsChunk; p.chunks_per_frame = w.chunks_per_frame;
+  p.chunk = w.chunk; p.chunks_per_frame = w.chunks_per_frame;
   p.scale = scale; p.threshold = gap_threshold_nats;
   p.key_mean = key_mean; p.rec = rec;
   char *base = static_cast<char *>(workspace);
