@@ -249,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void bounds_pass1(BoundsParams p, Produce
   if (threadIdx.x == 0) p.ws_qmax[(int64_t)bh * NC + c] = m;
 }
 
-constexpr int kHeadThreads = 512;
+constexpr int kHeadThreads = 1024;
 constexpr int kHeadLdsFloats = 12288;   // frame sums staged in LDS up to this size (48 KB)
 
 // Per head: the frame key sums (each the sum of its chunks' partial sums in
