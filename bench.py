@@ -279,7 +279,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only (the path shards by heads with no "
+        print("bench.py: the library runs on one GPU (the path would shard by heads with no "
               "exchange inside it; multi-GPU runs are not part of it). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
@@ -304,7 +304,7 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": nbytes, "launches": 3}), flush=True)
         return
     fs.lib()
-    w = workloads.config(args.workload)
+    w = workloads.workload(args.workload)
     print(f"[bench] workload {args.workload} {w.name}: generating inputs", file=sys.stderr, flush=True)
     q, k, v = workloads.make_inputs(w, seed=0)
     td = torch.bfloat16 if w.dtype == "bf16" else torch.float32

@@ -23,6 +23,6 @@ def config_inputs():
 
     def get(i):
         if i not in _INPUT_CACHE:
-            _INPUT_CACHE[i] = workloads.make_inputs(workloads.config(i), seed=0)
+            _INPUT_CACHE[i] = workloads.make_inputs(workloads.workload(i), seed=0)
         return _INPUT_CACHE[i]
     return get

@@ -35,7 +35,7 @@ def test_struct_layouts():
 
 @pytest.mark.parametrize("i", [1, 2, 3, 4, 5])
 def test_plan_bit_exact_vs_oracle_on_workloads(i):
-    w = workloads.config(i)
+    w = workloads.workload(i)
     rp, ci = fs.plan(w)
     orp, oci = oracle.plan_bruteforce(oracle.MaskGeometry(*w.mask_tuple()))
     assert np.array_equal(rp.numpy(), orp)
@@ -149,7 +149,7 @@ def test_head_bounds_validation():
 def test_workspace_bytes():
     L = fs.lib()
     s = F.Shape(1, 4, 48960, 128, 1)
-    m = F.to_mask(workloads.config(5))
+    m = F.to_mask(workloads.workload(5))
     assert L.fsattn_head_bounds_workspace_bytes(ctypes.byref(s), ctypes.byref(m)) > 4 * 128 * 6 * 4
     bad = F.Shape(1, 4, 48961, 128, 1)
     assert L.fsattn_head_bounds_workspace_bytes(ctypes.byref(bad), ctypes.byref(m)) == 0
@@ -173,13 +173,13 @@ def test_forward_validation():
 
 def test_launch_info_choices():
     for i in (2, 3, 4, 5):
-        w = workloads.config(i)
+        w = workloads.workload(i)
         waves, rows, kstep, wgs, lds = fs.launch_info((w.batch, w.heads, w.seq_len, w.head_dim), fs.BF16, w)
         assert w.tokens_per_frame % rows == 0                  # a wave tile never straddles frames
         tiles = -(-w.tokens_per_frame // (waves * rows))       # the last tile of a frame may be ragged
         assert wgs == w.batch * w.heads * w.num_frames * tiles
         assert lds <= 160 * 1024
-    w = workloads.config(3)
+    w = workloads.workload(3)
     # an explicit rows-per-wave that does not divide the frame span (3600 = 56 * 64 + 16) is
     # accepted: a frame's last wave runs partly past the frame's end and stores only its live rows
     waves, rows, _, wgs, _ = fs.launch_info((1, 5, 32400, 128), fs.BF16, w, fs.make_flags(waves=4, rows_per_wave=64))
@@ -188,7 +188,7 @@ def test_launch_info_choices():
     assert (waves, rows) == (2, 48)
     with pytest.raises(fs.FsattnError):           # 5-wave workgroups are not built
         fs.launch_info((1, 5, 32400, 128), fs.BF16, w, fs.make_flags(waves=5, rows_per_wave=48))
-    w2 = workloads.config(2)
+    w2 = workloads.workload(2)
     shape2 = (w2.batch, w2.heads, w2.seq_len, w2.head_dim)
     for ring, kstep, lds_expect in ((2, 32, 2 * 2 * 32 * 256), (3, 32, 3 * 2 * 32 * 256),
                                     (4, 32, 4 * 2 * 32 * 256), (2, 64, 2 * 2 * 64 * 256)):

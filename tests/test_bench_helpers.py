@@ -34,8 +34,8 @@ def test_partial_tile_share_matches_bruteforce():
 
 def test_partial_tile_share_on_the_workloads():
     for i in (1, 2, 4):
-        w = workloads.config(i)
+        w = workloads.workload(i)
         got = bench.partial_tile_share(w)
         partial, live = oracle.partial_blocks_if_tiled(oracle.MaskGeometry(*w.mask_tuple()), 128)
         assert (got["partial_tiles"], got["live_tiles"]) == (partial, live), i
-    assert bench.partial_tile_share(workloads.config(4))["partial_tiles"] == 0   # dense mask, T = 8 tiles
+    assert bench.partial_tile_share(workloads.workload(4))["partial_tiles"] == 0   # dense mask, T = 8 tiles

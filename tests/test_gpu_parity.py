@@ -79,7 +79,7 @@ def _sample_rows(w, per_frame, seed):
 @pytest.mark.parametrize("i", [1, 2, 3, 4, 5])
 def test_plan_device_bit_exact_on_workloads(dev, i):
     """fsattn_plan_device writes the host plan's arrays element for element."""
-    w = workloads.config(i)
+    w = workloads.workload(i)
     _say(f"[plan-device] {w.name}")
     rp, ci = fs.plan(w)
     dp = fs.plan_on_device(w, dev)
@@ -112,7 +112,7 @@ def test_plan_device_bit_exact_on_random_geometries(dev):
 
 @pytest.mark.parametrize("i", [1, 2, 3, 4, 5])
 def test_head_bounds_parity(dev, config_inputs, i):
-    w = workloads.config(i)
+    w = workloads.workload(i)
     _say(f"[bounds] workload {i} {w.name}")
     q, k, v = config_inputs(i)
     td = _tdtype(w)
@@ -131,7 +131,7 @@ def test_head_bounds_parity(dev, config_inputs, i):
 
 
 def test_head_bounds_deterministic(dev, config_inputs):
-    w = workloads.config(2)
+    w = workloads.workload(2)
     q, k, _ = config_inputs(2)
     qd, kd = _to_dev(q, torch.bfloat16, dev), _to_dev(k, torch.bfloat16, dev)
     a = fs.head_bounds(qd, kd, w)
@@ -194,7 +194,7 @@ def test_forward_dealing_is_bitwise_neutral(dev, config_inputs, i):
     """How the tiles are dealt to the XCDs (whole (frame, head) groups, the
     library's chunks, single tiles, a chunk larger than a group) changes only
     where each tile runs: the outputs are bitwise equal."""
-    w = workloads.config(i)
+    w = workloads.workload(i)
     q, k, v = config_inputs(i)
     qd, kd, vd = (_to_dev(x, torch.bfloat16, dev) for x in (q, k, v))
     dp = fs.device_plan(w, dev)
@@ -295,7 +295,7 @@ def test_forward_workload_parity(dev, config_inputs, i):
     default). Workload 1 is compared on every element; the others on sampled
     rows (frame edges + random rows of every frame, all heads), plus
     properties on every row: finite, and inside the range of V."""
-    w = workloads.config(i)
+    w = workloads.workload(i)
     _say(f"[fwd] workload {i} {w.name}")
     q, k, v = config_inputs(i)
     out, bnd, _ = _run(w, q, k, v, dev)
@@ -354,7 +354,7 @@ def test_forward_mask_variant_full_size(dev, config_inputs, variant):
     all 20,160 keys), with reference frames 0-1, and with global reference
     frames 0-2, in the library's default launch: bounds against the oracle,
     and sampled rows of every frame against it."""
-    w = dataclasses.replace(workloads.config(2), ref_queries_global=variant[0], ref_count=variant[1])
+    w = dataclasses.replace(workloads.workload(2), ref_queries_global=variant[0], ref_count=variant[1])
     _say(f"[fwd-variant] {w.name} ref_queries_global={variant[0]} ref_count={variant[1]}")
     q, k, v = config_inputs(2)
     out, bnd, _ = _run(w, q, k, v, dev)
@@ -373,7 +373,7 @@ def test_forward_mask_variant_full_size(dev, config_inputs, variant):
 
 
 def test_online_and_fixed_agree_on_eligible_heads(dev, config_inputs):
-    w = workloads.config(2)
+    w = workloads.workload(2)
     q, k, v = config_inputs(2)
     on, _, _ = _run(w, q, k, v, dev, flags=fs.make_flags("online"))
     fx, bnd, _ = _run(w, q, k, v, dev, flags=fs.make_flags("fixed"))
@@ -382,7 +382,7 @@ def test_online_and_fixed_agree_on_eligible_heads(dev, config_inputs):
 
 
 def test_stressed_heads_fall_back_and_stay_finite(dev, config_inputs):
-    w = workloads.config(4)
+    w = workloads.workload(4)
     q, k, v = config_inputs(4)
     auto, bnd, _ = _run(w, q, k, v, dev)
     elig = bnd.host()["eligible"][0]
@@ -398,7 +398,7 @@ def test_stressed_heads_fall_back_and_stay_finite(dev, config_inputs):
 
 
 def test_forward_deterministic(dev, config_inputs):
-    w = workloads.config(2)
+    w = workloads.workload(2)
     q, k, v = config_inputs(2)
     td = torch.bfloat16
     qd, kd, vd = (_to_dev(x, td, dev) for x in (q, k, v))
@@ -460,7 +460,7 @@ def test_prior_art_comparator_parity(dev, case):
 def test_prior_art_comparator_on_workloads(dev, config_inputs, i):
     """Full-size workloads: sampled rows against the oracle, and every row
     against fsattn_forward within bf16 rounding."""
-    w = workloads.config(i)
+    w = workloads.workload(i)
     q, k, v = config_inputs(i)
     qd, kd, vd = (_to_dev(x, torch.bfloat16, dev) for x in (q, k, v))
     _say(f"[prior-art] workload {i}")
@@ -544,7 +544,7 @@ def test_produce_then_forward_full_size(dev):
     element; the bound records bit for bit against fsattn_head_bounds on the
     outputs and against the oracle; sampled output rows of every frame
     against the oracle's attention on the produced Q, K, V."""
-    w = workloads.config(5)
+    w = workloads.workload(5)
     _say(f"[produce] {w.name} full size, then forward")
     x = workloads.make_producer_inputs(w, seed=6)
     qkv, views = _packed_views((x["q"], x["k"], x["v"]), torch.bfloat16, dev)

@@ -44,7 +44,7 @@ def test_plan_matches_hand_derived_golden():
 
 def test_plan_sizes_of_workloads_match_hand_counts():
     gold = {w["name"]: w for w in json.load(open(os.path.join(GOLDEN, "workload_plan_sizes.json")))["workloads"]}
-    for w in workloads.CONFIGS:
+    for w in workloads.WORKLOADS:
         g = _geom(w.mask_tuple())
         want = gold[w.name]
         assert [len(oracle.live_frames(g, f)) for f in range(g.F)] == want["live_frames_per_frame"]
@@ -57,7 +57,7 @@ def test_plan_sizes_of_workloads_match_hand_counts():
 @pytest.mark.slow
 def test_plan_sizes_of_large_workloads_bruteforce():
     gold = {w["name"]: w for w in json.load(open(os.path.join(GOLDEN, "workload_plan_sizes.json")))["workloads"]}
-    for w in workloads.CONFIGS:
+    for w in workloads.WORKLOADS:
         g = _geom(w.mask_tuple())
         rp, ci = oracle.plan_bruteforce(g)
         assert len(ci) == gold[w.name]["nnz"]
@@ -383,14 +383,14 @@ def test_bound_audit_exhaustive_small():
 
 def test_bound_audit_workload1_exhaustive(config_inputs):
     q, k, _ = config_inputs(1)
-    rec, stats = _check_bound_audit(q, k, _geom(workloads.config(1).mask_tuple()))
+    rec, stats = _check_bound_audit(q, k, _geom(workloads.workload(1).mask_tuple()))
     assert rec["eligible"].all()
 
 
 @pytest.mark.parametrize("i", [2, 3, 5])
 def test_bound_audit_workloads_sampled_rows_and_eligibility(config_inputs, i):
     q, k, _ = config_inputs(i)
-    w = workloads.config(i)
+    w = workloads.workload(i)
     g = _geom(w.mask_tuple())
     rows = np.random.default_rng(i).choice(g.N, 24, replace=False)
     rec, _ = _check_bound_audit(q, k, g, rows=rows)
@@ -402,7 +402,7 @@ def test_workload3_needs_mean_centring(config_inputs):
     """Keys carry a per-head mean offset; the raw (uncentred) bound is above 30
     nats while the centred one qualifies - the reason centring is done."""
     q, k, _ = config_inputs(3)
-    g = _geom(workloads.config(3).mask_tuple())
+    g = _geom(workloads.workload(3).mask_tuple())
     rec = oracle.head_bounds_ref(q, k, g)
     scale = 1 / math.sqrt(128)
     raw_kmax = np.sqrt((np.asarray(k, np.float64) ** 2).sum(-1)).max(-1)
@@ -413,7 +413,7 @@ def test_workload3_needs_mean_centring(config_inputs):
 
 def test_workload4_stressed_heads_fail_eligibility(config_inputs):
     q, k, _ = config_inputs(4)
-    g = _geom(workloads.config(4).mask_tuple())
+    g = _geom(workloads.workload(4).mask_tuple())
     rec = oracle.head_bounds_ref(q, k, g)
     elig = rec["eligible"][0]
     assert [h for h in range(16) if not elig[h]] == list(workloads.STRESSED_HEADS)
@@ -427,16 +427,16 @@ def test_workload4_stressed_heads_fail_eligibility(config_inputs):
 
 
 def test_live_flops_closed_form():
-    assert oracle.live_flops(_geom(workloads.config(2).mask_tuple()), 1, 8, 128) == 4 * 128 * 8 * 117 * 960 * 960
-    assert oracle.live_flops(_geom(workloads.config(5).mask_tuple()), 1, 4, 128) == 2727346176000
+    assert oracle.live_flops(_geom(workloads.workload(2).mask_tuple()), 1, 8, 128) == 4 * 128 * 8 * 117 * 960 * 960
+    assert oracle.live_flops(_geom(workloads.workload(5).mask_tuple()), 1, 4, 128) == 2727346176000
     # global reference frame 0 of 21 frames with window +-2: frame 0 sees 21
     # frames instead of 3, so 117 - 3 + 21 = 135 frame pairs
-    g = _geom(workloads.config(2).mask_tuple()[:7] + (1,))
+    g = _geom(workloads.workload(2).mask_tuple()[:7] + (1,))
     assert oracle.live_flops(g, 1, 8, 128) == 4 * 128 * 8 * 135 * 960 * 960
     # reference frames 0-1 of 21 with window +-2: frames 0..3 see 3, 4, 5, 6
     # frames, 4..18 see 5 + 2, and 19, 20 (window clamped) 4 + 2 and 3 + 2:
     # 18 + 15 * 7 + 11 = 134 frame pairs
-    g = _geom(workloads.config(2).mask_tuple()[:7] + (0, 2))
+    g = _geom(workloads.workload(2).mask_tuple()[:7] + (0, 2))
     assert [len(oracle.live_frames(g, f)) for f in (0, 1, 2, 3, 4, 18, 19, 20)] == [3, 4, 5, 6, 7, 7, 6, 5]
     assert oracle.live_flops(g, 1, 8, 128) == 4 * 128 * 8 * 134 * 960 * 960
 

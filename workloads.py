@@ -61,7 +61,7 @@ class Workload:
 
 # The five workloads. Sizes are one GPU's share of heads at the full
 # sequence length.
-CONFIGS = [
+WORKLOADS = [
     Workload("tiny_f32_5x48", 1, 2, 5, 48, 64, "f32", 1, 1, 0, 16, 16,
              "none", "5 frames x 48 tokens, window +-1 + reference frame 0, blocks 16, fp32"),
     Workload("bf16_21x960", 1, 8, 21, 960, 128, "bf16", 2, 2, 0, 64, 64,
@@ -82,9 +82,9 @@ STRESS_FACTOR = 40.0
 RMS_EPS = 1e-6
 
 
-def config(i: int) -> Workload:
+def workload(i: int) -> Workload:
     """Workload by its 1-based number (1..5)."""
-    return CONFIGS[i - 1]
+    return WORKLOADS[i - 1]
 
 
 def make_workload(name, batch, heads, num_frames, tokens_per_frame, head_dim,
