@@ -6,14 +6,18 @@ One step = one pass of the whole path over one batch of synthetic input:
   one stream.
 Inputs are resident in HBM before timing starts. The metric counts live-block
 FLOPs only: 4 * d per live (query, key) pair (QK^T and PV), summed over
-every head.
+every head. The default workload is the largest single-GPU one (6 frames x
+8160 tokens, 4 heads, d = 128, bf16); workloads 2 and 3 are measured in the
+same run with the same protocol and reported under "workloads".
 
 Prints ONE JSON line. The roofline object describes the dominant kernel
 (the forward) from HIP events recorded around each of its launches on the
-stream it runs on; `traffic` comes from the rocprofv3 counter summary in
-profiles/ when that summary was taken on the current kernel source.
-The CPU baseline times the fp64 oracle on a bounded row sample on the
-host cores (rank 0, N = 1 only).
+stream it runs on (median and minimum over the timed steps); `traffic` and
+`mfma_busy_pct` come from the rocprofv3 summaries in profiles/ when those
+were taken on the current kernel source. Bounds and producer repetitions
+each follow a 512 MiB scratch write, so that their inputs are not served
+from the 256 MB last-level cache. The CPU baseline times the fp64 oracle on
+a bounded row sample on the host cores (rank 0, N = 1 only).
 """
 from __future__ import annotations
 
@@ -43,22 +47,46 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
-    """HBM bytes per forward launch from profiles/forward_traffic_<workload>.txt
-    (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), or None if
+def _read_summary(name: str):
+    """key: value pairs of profiles/<name>.txt (comments stripped), or None if
     absent or taken on a different kernel source."""
-    path = os.path.join(ROOT, "profiles", f"forward_traffic_{workload}.txt")
+    path = os.path.join(ROOT, "profiles", name + ".txt")
     if not os.path.exists(path):
         return None
     kv = {}
     for line in open(path):
-        if ":" in line and not line.lstrip().startswith("#"):
+        line = line.split("#", 1)[0] if not line.lstrip().startswith("#") else ""
+        if ":" in line:
             a, b = line.split(":", 1)
             kv[a.strip()] = b.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+    src = kv.get("kernel_source_sha256_16")
+    if src is None:   # (the hash may sit in a comment line)
+        for line in open(path):
+            if "kernel_source_sha256_16:" in line:
+                src = line.split("kernel_source_sha256_16:", 1)[1].split()[0]
+    if src != kernel_source_hash():
         return None
+    return kv
+
+
+def read_traffic(workload: str):
+    """HBM bytes per forward launch from profiles/forward_traffic_<workload>.txt
+    (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), or None if
+    absent or taken on a different kernel source."""
+    kv = _read_summary(f"forward_traffic_{workload}")
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv["hbm_bytes_per_launch"]) if kv else None
+    except (KeyError, ValueError):
+        return None
+
+
+def read_mfma_busy(workload: str):
+    """Percent of SIMD cycles the matrix unit was busy under the forward
+    (SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs x active cycles), from
+    profiles/forward_counters_<workload>.txt, or None."""
+    kv = _read_summary(f"forward_counters_{workload}")
+    try:
+        return round(100.0 * float(kv["mfma_busy_fraction"]), 1) if kv else None
     except (KeyError, ValueError):
         return None
 
@@ -175,13 +203,20 @@ def mask_variant_timing(w, qd, kd, vd, reps: int = 10):
     return out
 
 
-def producer_timing(w, dev, bounds_ms: float, reps: int = 20):
+def flush_llc(buf):
+    """Write the whole scratch buffer (512 MiB, twice the last-level cache),
+    so the next kernel's inputs come from HBM."""
+    buf.fill_(0x5A)
+
+
+def producer_timing(w, dev, bounds_ms: float, flush_buf, reps: int = 20):
     """fsattn_produce at the workload's shape, from a token-major packed
     projection output [B, N, 3, H, d]: RMSNorm(gamma) and rotary embedding of
     Q and K, Q/K/V written head-major, and the bound records. Algorithmic
     bytes: Q, K, V read and written once, plus the second read of K that the
     key-norm maximum needs after the key mean (7 rows of d per token and
-    head). Reported beside the separate bounds call it replaces."""
+    head). Each repetition follows a scratch write that evicts the
+    last-level cache. Reported beside the separate bounds call it replaces."""
     import numpy as np
     import torch
     import frame_block_sparse_amd as fs
@@ -200,19 +235,117 @@ def producer_timing(w, dev, bounds_ms: float, reps: int = 20):
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     fs.produce(*views, w, gq, gk, 1e-6, cs, sn, out=out, workspace=ws, bounds=bnd)
     for a, b in ev:
+        flush_llc(flush_buf)
         a.record()
         fs.produce(*views, w, gq, gk, 1e-6, cs, sn, out=out, workspace=ws, bounds=bnd)
         b.record()
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in ev)
-    avg = sum(ms) / len(ms)
+    med = ms[len(ms) // 2]
     esz = 2 if w.dtype == "bf16" else 4
     nbytes = 7.0 * B * H * N * d * esz
-    return {"avg_ms": round(avg, 5), "algorithmic_bytes": nbytes, "GBps": round(nbytes / (avg * 1e-3) / 1e9, 1),
-            "peak_GBps": PEAK_HBM_GBS, "frac": round(nbytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "separate_bounds_ms": round(bounds_ms, 5),
+    return {"median_ms": round(med, 5), "min_ms": round(ms[0], 5), "algorithmic_bytes": nbytes,
+            "GBps": round(nbytes / (med * 1e-3) / 1e9, 1), "peak_GBps": PEAK_HBM_GBS,
+            "frac": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "separate_bounds_ms": round(bounds_ms, 5), "llc_flushed": True,
             "what": "RMSNorm(gamma) + rotary embedding of Q, K from a token-major QKV projection output, "
                     "Q/K/V written head-major, bound records of the values written (fsattn_produce)"}
+
+
+def bounds_timing(w, qd, kd, mask, flush_buf, reps: int = 50):
+    """fsattn_head_bounds, each repetition after a scratch write that evicts
+    the last-level cache; median and minimum of event-timed launches. The
+    rate is algorithmic bytes (Q and K read once) over time; the kernels
+    read K a second time (mostly from the last-level cache) after the key
+    mean is known."""
+    import torch
+    import frame_block_sparse_amd as fs
+    dev = qd.device
+    ws = torch.empty(max(1, fs.head_bounds_workspace_bytes(qd, mask)), dtype=torch.uint8, device=dev)
+    bnd = fs.Bounds(torch.empty((w.batch, w.heads, w.head_dim), dtype=torch.float32, device=dev),
+                    torch.empty((w.batch, w.heads, 8), dtype=torch.float32, device=dev))
+    fs.head_bounds(qd, kd, mask, workspace=ws, out=bnd)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        flush_llc(flush_buf)
+        a.record()
+        fs.head_bounds(qd, kd, mask, workspace=ws, out=bnd)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    med = ms[len(ms) // 2]
+    esz = 2 if w.dtype == "bf16" else 4
+    nbytes = 2.0 * w.batch * w.heads * w.seq_len * w.head_dim * esz
+    return {"median_ms": round(med, 5), "min_ms": round(ms[0], 5), "algorithmic_bytes": nbytes,
+            "GBps": round(nbytes / (med * 1e-3) / 1e9, 1), "peak_GBps": PEAK_HBM_GBS,
+            "frac": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "llc_flushed": True,
+            "launches": 4}
+
+
+def sampled_error(w, q, k, v, out, per_frame: int = 16, seed: int = 7):
+    """max |O_gpu - O_oracle| over sampled rows (frame edges and `per_frame`
+    random rows of every frame, every (batch, head)), and max |O_gpu| over
+    every element. The GPU tests compare every element; this is the
+    benchmark's own check of the output it timed."""
+    import numpy as np
+    import oracle
+    g = oracle.MaskGeometry(*w.mask_tuple())
+    rng = np.random.default_rng(seed)
+    rows = []
+    for f in range(g.F):
+        a = f * g.T
+        rows += [a, a + g.T - 1] + list(a + rng.choice(g.T, min(per_frame, g.T), replace=False))
+    rows = np.unique(np.array(rows))
+    ref, _ = oracle.attention_live_ref(q, k, v, g, rows=rows)
+    got = out[:, :, rows].float().cpu().numpy()
+    return float(np.abs(got - ref).max()), float(out.float().abs().max().item()), int(len(rows))
+
+
+def forward_timing(w, qd, kd, vd, dplan, bnd, flags, out, reps: int = 50, warm: int = 5):
+    """Event-timed forward launches (library default launch unless flags say
+    otherwise): median and minimum over `reps`."""
+    import torch
+    import frame_block_sparse_amd as fs
+    for _ in range(warm):
+        fs.forward(qd, kd, vd, dplan, bnd, flags=flags, out=out)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        fs.forward(qd, kd, vd, dplan, bnd, flags=flags, out=out)
+        b.record()
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) for a, b in ev)
+
+
+def workload_record(idx, dev, flush_buf, flags, reps: int = 50):
+    """One workload measured with the headline's protocol minus the step
+    loop: forward median/min over `reps` event-timed launches, flushed
+    bounds, eligibility, sampled error against the oracle."""
+    import torch
+    import frame_block_sparse_amd as fs
+    from frame_block_sparse_amd import fsattn as F
+    import workloads
+    w = workloads.workload(idx)
+    print(f"[bench] workload {idx} {w.name}: generating inputs", file=sys.stderr, flush=True)
+    q, k, v = workloads.make_inputs(w, seed=0)
+    td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    qd, kd, vd = (torch.from_numpy(x).to(td).to(dev) for x in (q, k, v))
+    od = torch.empty_like(qd)
+    mask = F.to_mask(w)
+    _, nnz = fs.plan_size(mask)
+    live_flops = 4.0 * w.head_dim * w.batch * w.heads * nnz * w.block_q * w.block_k
+    dplan = fs.plan_on_device(mask, dev)
+    bnd = fs.head_bounds(qd, kd, mask)
+    ms = forward_timing(w, qd, kd, vd, dplan, bnd, flags, od, reps=reps)
+    med = ms[len(ms) // 2]
+    err, omax, nrows = sampled_error(w, q, k, v, od)
+    tf = live_flops / (med * 1e-3) / 1e12
+    return {"workload": w.name, "live_gflop": round(live_flops / 1e9, 3), "t_fwd_ms_median": round(med, 5),
+            "t_fwd_ms_min": round(ms[0], 5), "tflops": round(tf, 1), "pct_peak_nominal": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+            "tflops_at_min": round(live_flops / (ms[0] * 1e-3) / 1e12, 1),
+            "mfma_busy_pct": read_mfma_busy(w.name), "eligible_heads": int(bnd.host()["eligible"].sum()),
+            "bounds": bounds_timing(w, qd, kd, mask, flush_buf), "max_abs_err": err, "max_abs_out": omax,
+            "err_rows_sampled": nrows, "partial_tiles_if_128": partial_tile_share(w)}
 
 
 def cpu_baseline(w, q, k, v, budget_s: float):
@@ -259,9 +392,13 @@ def cpu_baseline(w, q, k, v, budget_s: float):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, help="1..5 (default 2: bf16, 21 frames x 960 tokens)")
+    ap.add_argument("--workload", type=int, default=5,
+                    help="1..5 (default 5: bf16, 6 frames x 8160 tokens, the largest single-GPU workload)")
+    ap.add_argument("--extra-workloads", default="2,3",
+                    help="comma-separated workloads also measured (forward median/min, flushed bounds, error); "
+                         "empty for none")
     ap.add_argument("--waves", type=int, default=0)
     ap.add_argument("--rows", type=int, default=0)
     ap.add_argument("--kstep", type=int, default=0)
@@ -272,6 +409,9 @@ def main():
                     help="untimed forward launches before the warmup steps, so that the GPU clocks have "
                          "ramped up after the host-side input generation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the timed steps (for profiling runs): no comparator, producer, mask variants, "
+                         "extra workloads or oracle check")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device-to-device copy of 512 MiB three times (the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -283,9 +423,7 @@ def main():
               "exchange inside it; multi-GPU runs are not part of it). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
-    import ctypes
     import frame_block_sparse_amd as fs
     from frame_block_sparse_amd import fsattn as F
     import workloads
@@ -310,6 +448,7 @@ def main():
     td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     qd, kd, vd = (torch.from_numpy(x).to(td).to(dev) for x in (q, k, v))
     od = torch.empty_like(qd)
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     mask = F.to_mask(w)
     nqb, nnz = fs.plan_size(mask)
     flags = fs.make_flags(args.mode, waves=args.waves, rows_per_wave=args.rows, key_step=args.kstep, ring=args.ring)
@@ -353,29 +492,21 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
-    fwd_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.warmup, total)]
+    fwd_ms = sorted(ev[i][0].elapsed_time(ev[i][1]) for i in range(args.warmup, total))
     fwd_avg = sum(fwd_ms) / len(fwd_ms)
-    # plan and bounds launch times (untimed loop, events around each)
-    aux = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
-    for a, b, c in aux:
+    fwd_med = fwd_ms[len(fwd_ms) // 2]
+    # plan launch times (untimed loop, events around each)
+    aux = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(args.steps)]
+    for a, b in aux:
         a.record()
         fs.plan_on_device(mask, out=dplan)
         b.record()
-        fs.head_bounds(qd, kd, mask, workspace=ws, out=bnd)
-        c.record()
     torch.cuda.synchronize()
-    plan_ms = [a.elapsed_time(b) for a, b, _ in aux]
-    bnd_ms = [b.elapsed_time(c) for _, b, c in aux]
-    bnd_avg = sum(bnd_ms) / len(bnd_ms)
-    achieved = live_flops / (fwd_avg * 1e-3) / 1e12
-    ref_mfma = mfma_reference(dev) if w.dtype == "bf16" else None
-    prior = prior_art_timing(w, qd, kd, vd, fwd_avg, live_flops) if w.dtype == "bf16" else None
+    plan_ms = sorted(a.elapsed_time(b) for a, b in aux)
     value = live_flops / (ms_step * 1e-3) / 1e12
-    producer = producer_timing(w, dev, bnd_avg)
-    variants = mask_variant_timing(w, qd, kd, vd) if w.dtype == "bf16" else None
+    achieved = live_flops / (fwd_avg * 1e-3) / 1e12
     elig = bnd.host()["eligible"]
     esz = 2 if w.dtype == "bf16" else 4
-    bounds_bytes = 2.0 * w.batch * w.heads * w.seq_len * w.head_dim * esz
 
     result = {
         "metric": METRIC,
@@ -405,18 +536,36 @@ def main():
             "kernel": "fwd_bf16_kernel" if w.dtype == "bf16" else "fwd_f32_kernel",
             "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": read_traffic(w.name),
-            "avg_launch_ms": round(fwd_avg, 5), "algorithmic_flop_per_launch": live_flops,
-            "measured_mfma_peak": ref_mfma,
-            "frac_of_measured_peak": round(achieved / ref_mfma["tflops"], 4) if ref_mfma else None,
+            "avg_launch_ms": round(fwd_avg, 5), "t_fwd_ms_median": round(fwd_med, 5),
+            "t_fwd_ms_min": round(fwd_ms[0], 5),
+            "frac_at_median": round(live_flops / (fwd_med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "frac_at_min": round(live_flops / (fwd_ms[0] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "algorithmic_flop_per_launch": live_flops, "mfma_busy_pct": read_mfma_busy(w.name),
         },
-        "partial_tiles_if_128": partial_tile_share(w),
-        "prior_art": prior,
-        "plan": {"avg_ms": round(sum(plan_ms) / len(plan_ms), 5), "nnz": nnz},
-        "bounds": {"avg_ms": round(bnd_avg, 5), "algorithmic_bytes": bounds_bytes,
-                   "GBps": round(bounds_bytes / (bnd_avg * 1e-3) / 1e9, 1), "peak_GBps": PEAK_HBM_GBS},
-        "producer": producer,
-        "mask_variants": variants,
+        "plan": {"median_ms": round(plan_ms[len(plan_ms) // 2], 5), "nnz": nnz},
     }
+    if not args.no_extras:
+        print("[bench] bounds (flushed), reference MFMA loop, comparator, producer, variants", file=sys.stderr,
+              flush=True)
+        bounds = bounds_timing(w, qd, kd, mask, flush_buf)
+        result["bounds"] = bounds
+        if w.dtype == "bf16":
+            ref_mfma = mfma_reference(dev)
+            result["roofline"]["measured_mfma_peak"] = ref_mfma
+            result["roofline"]["frac_of_measured_peak"] = round(achieved / ref_mfma["tflops"], 4)
+            result["prior_art"] = prior_art_timing(w, qd, kd, vd, fwd_avg, live_flops)
+            result["mask_variants"] = mask_variant_timing(w, qd, kd, vd)
+        result["producer"] = producer_timing(w, dev, bounds["median_ms"], flush_buf)
+        result["partial_tiles_if_128"] = partial_tile_share(w)
+        print("[bench] output check against the oracle (sampled rows)", file=sys.stderr, flush=True)
+        err, omax, nrows = sampled_error(w, q, k, v, od)
+        result["max_abs_err"] = err
+        result["max_abs_out"] = omax
+        result["err_rows_sampled"] = nrows
+        extra = [int(x) for x in args.extra_workloads.split(",") if x.strip()]
+        extra = [x for x in extra if x != args.workload]
+        if extra:
+            result["workloads"] = [workload_record(x, dev, flush_buf, flags) for x in extra]
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle, bounded sample)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_baseline_seconds)

@@ -64,7 +64,11 @@ Readings where the pages are silent (each also listed in the design notes):
 
 Parity status: every function below is pinned by tests that do not reuse
 its own arithmetic (brute force over tokens, closed forms, invariants,
-a library attention routine); none is "parity unpinned".
+a library attention routine, hand-worked values); none is "parity
+unpinned". In particular the row shift is pinned by brute force (it is at
+least every raw live logit of its row, and at most gap_est above the row's
+largest one) and by a hand value, and the eligibility threshold by hand
+heads whose gap estimate is just below, exactly at and just above 30 nats.
 """
 from __future__ import annotations
 
@@ -255,6 +259,54 @@ def attention_ref(q, k, v, g: MaskGeometry, scale: Optional[float] = None,
     return out, lse
 
 
+def attention_live_ref(q, k, v, g: MaskGeometry, scale: Optional[float] = None,
+                       rows: Optional[Sequence[int]] = None, chunk: int = 1024):
+    """The same plain masked softmax attention as attention_ref, in fp64,
+    with each row's sums taken over its live keys only: the terms of masked
+    keys are exactly zero in the definition, so leaving them out changes
+    nothing. A row's live keys depend only on its frame (token_mask is a
+    function of the two frame indices), so the rows of one frame share one
+    key list, which is read off the mask rows themselves (and checked to be
+    the same for every row of the chunk). torch's CPU fp64 matmul and exp
+    are used for their threads; this makes full-size workloads affordable.
+
+    Same arguments and results as attention_ref: (O (B, H, R, d),
+    lse (B, H, R)) as fp64 numpy arrays."""
+    import torch
+    q = np.asarray(q); k = np.asarray(k); v = np.asarray(v)
+    B, H, N, d = q.shape
+    assert N == g.N
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = len(rows)
+    qt = torch.from_numpy(np.ascontiguousarray(q)).to(torch.float64)
+    kt = torch.from_numpy(np.ascontiguousarray(k)).to(torch.float64)
+    vt = torch.from_numpy(np.ascontiguousarray(v)).to(torch.float64)
+    out = np.empty((B, H, R, d), dtype=np.float64)
+    lse = np.empty((B, H, R), dtype=np.float64)
+    frame_of = rows // g.T
+    for f in np.unique(frame_of):
+        pos = np.nonzero(frame_of == f)[0]              # positions in `rows` of frame f's rows
+        for s in range(0, len(pos), chunk):
+            pp = pos[s:s + chunk]
+            ri = rows[pp]
+            m = mask_rows(g, ri)
+            assert (m == m[0]).all()
+            live = torch.from_numpy(np.nonzero(m[0])[0])
+            for b in range(B):
+                for h in range(H):
+                    kl = kt[b, h].index_select(0, live)
+                    vl = vt[b, h].index_select(0, live)
+                    sc = scale * (qt[b, h].index_select(0, torch.from_numpy(ri)) @ kl.T)
+                    mx = sc.max(dim=1, keepdim=True).values
+                    p = torch.exp(sc - mx)
+                    l = p.sum(dim=1, keepdim=True)
+                    out[b, h, pp] = ((p @ vl) / l).numpy()
+                    lse[b, h, pp] = (mx[:, 0] + torch.log(l[:, 0])).numpy()
+    return out, lse
+
+
 def attention_online_ref(q, k, v, g: MaskGeometry, scale=None, key_block=None):
     """fp64 flash-style online softmax ("Unchaining the Softmax", Fig. 4,
     upper chain): for each query row walk its live keys in blocks, carry a
@@ -427,10 +479,3 @@ def rope_tables_1d(n, d, base=10000.0):
     i = np.arange(d // 2, dtype=np.float64)
     ang = np.arange(n, dtype=np.float64)[:, None] * base ** (-2.0 * i / d)[None, :]
     return np.cos(ang), np.sin(ang)
-
-
-def producer_bytes(batch, heads, seq_len, head_dim, elem_bytes):
-    """Algorithmic HBM bytes of one producer launch: Q, K and V read once and
-    written once (the per-head gammas and the angle tables are small and
-    not counted)."""
-    return 6 * batch * heads * seq_len * head_dim * elem_bytes

@@ -25,6 +25,12 @@ def _geom(t):
     return oracle.MaskGeometry(*t)
 
 
+# the two attention oracles: dense scores with -inf outside the mask, and the
+# same sums taken over each row's live keys only; every attention pin runs on both
+ATTN_IMPLS = [oracle.attention_ref, oracle.attention_live_ref]
+ATTN_IDS = ["dense", "live_keys"]
+
+
 def _rand_qkv(rng, B, H, N, d, kscale=1.0):
     q = rng.standard_normal((B, H, N, d))
     k = kscale * rng.standard_normal((B, H, N, d))
@@ -148,38 +154,41 @@ def _bruteforce_attention(q, k, v, F, T, wb, wa, r, scale, rg=0, nr=0):
 @pytest.mark.parametrize("geom", [(3, 4, 1, 1, 0), (4, 3, 0, 1, 2), (5, 2, 1, 0, -1), (2, 5, 0, 0, 1),
                                   (4, 3, 0, 0, 2, 1), (5, 2, 1, 0, 0, 1), (6, 2, 0, 0, 1, 0, 3),
                                   (5, 3, 1, 0, 2, 1, 2)])
-def test_attention_matches_bruteforce_loops(geom):
+@pytest.mark.parametrize("attn", ATTN_IMPLS, ids=ATTN_IDS)
+def test_attention_matches_bruteforce_loops(attn, geom):
     F, T, wb, wa, r = geom[:5]
     rg = geom[5] if len(geom) > 5 else 0
     nr = geom[6] if len(geom) > 6 else 0
     rng = np.random.default_rng(F * 100 + T)
     q, k, v = _rand_qkv(rng, 1, 2, F * T, 5)
     g = oracle.MaskGeometry(F, T, wb, wa, r, 16, 16, rg, nr)     # blocks unused by attention_ref
-    o, lse = oracle.attention_ref(q, k, v, g, scale=0.7)
+    o, lse = attn(q, k, v, g, scale=0.7)
     ob, lb = _bruteforce_attention(q, k, v, F, T, wb, wa, r, 0.7, rg, nr)
     np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
     np.testing.assert_allclose(lse, lb, rtol=0, atol=1e-12)
 
 
-def test_attention_dense_matches_torch_sdpa():
+@pytest.mark.parametrize("attn", ATTN_IMPLS, ids=ATTN_IDS)
+def test_attention_dense_matches_torch_sdpa(attn):
     import torch
     rng = np.random.default_rng(3)
     F, T, d = 4, 24, 16
     q, k, v = _rand_qkv(rng, 2, 3, F * T, d)
     g = oracle.MaskGeometry(F, T, F, F, 0, 16, 16)       # window covers everything
-    o, _ = oracle.attention_ref(q, k, v, g)
+    o, _ = attn(q, k, v, g)
     ref = torch.nn.functional.scaled_dot_product_attention(
         torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v)).numpy()
     np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
 
 
-def test_attention_windowed_matches_torch_sdpa_with_boolean_mask():
+@pytest.mark.parametrize("attn", ATTN_IMPLS, ids=ATTN_IDS)
+def test_attention_windowed_matches_torch_sdpa_with_boolean_mask(attn):
     import torch
     rng = np.random.default_rng(4)
     F, T, d = 6, 16, 8
     q, k, v = _rand_qkv(rng, 1, 2, F * T, d)
     g = oracle.MaskGeometry(F, T, 1, 2, 5, 16, 16)
-    o, _ = oracle.attention_ref(q, k, v, g, scale=0.3)
+    o, _ = attn(q, k, v, g, scale=0.3)
     fr = np.arange(F * T) // T
     allowed = np.zeros((F * T, F * T), dtype=bool)
     for i in range(F * T):
@@ -191,44 +200,47 @@ def test_attention_windowed_matches_torch_sdpa_with_boolean_mask():
     np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
 
 
-def test_attention_closed_forms():
+@pytest.mark.parametrize("attn", ATTN_IMPLS, ids=ATTN_IDS)
+def test_attention_closed_forms(attn):
     rng = np.random.default_rng(5)
     F, T, d = 5, 16, 8
     g = oracle.MaskGeometry(F, T, 1, 1, 0, 16, 16)
     q, k, v = _rand_qkv(rng, 1, 2, F * T, d)
     # Q = 0: every live key has weight 1/|live|, so O_i is the mean of V over row i's live keys
-    o, lse = oracle.attention_ref(np.zeros_like(q), k, v, g)
+    o, lse = attn(np.zeros_like(q), k, v, g)
     for i in range(F * T):
         live = [j for j in range(F * T) if j // T in oracle.live_frames(g, i // T)]
         np.testing.assert_allclose(o[:, :, i], v[:, :, live].mean(axis=2), atol=1e-12)
         np.testing.assert_allclose(lse[:, :, i], math.log(len(live)), atol=1e-12)
     # V rows all equal to c: O = c
     c = rng.standard_normal(d)
-    o, _ = oracle.attention_ref(q, k, np.broadcast_to(c, v.shape), g)
+    o, _ = attn(q, k, np.broadcast_to(c, v.shape), g)
     np.testing.assert_allclose(o, np.broadcast_to(c, o.shape), atol=1e-12)
     # common key offset k_j + c adds q_i . c to every logit of row i: O unchanged
-    o0, lse0 = oracle.attention_ref(q, k, v, g)
-    o1, lse1 = oracle.attention_ref(q, k + 3.0 * c, v, g)
+    o0, lse0 = attn(q, k, v, g)
+    o1, lse1 = attn(q, k + 3.0 * c, v, g)
     np.testing.assert_allclose(o1, o0, atol=1e-11)
     np.testing.assert_allclose(lse1 - lse0, 3.0 * (q @ c) / math.sqrt(d), atol=1e-10)
     # permuting tokens inside each frame permutes the output rows the same way
     perm = np.concatenate([f * T + rng.permutation(T) for f in range(F)])
-    o2, _ = oracle.attention_ref(q[:, :, perm], k[:, :, perm], v[:, :, perm], g)
+    o2, _ = attn(q[:, :, perm], k[:, :, perm], v[:, :, perm], g)
     np.testing.assert_allclose(o2, o0[:, :, perm], atol=1e-12)
     # scaling q by a with scale 1/a is the same softmax
-    o3, _ = oracle.attention_ref(2.0 * q, k, v, g, scale=0.5 / math.sqrt(d))
+    o3, _ = attn(2.0 * q, k, v, g, scale=0.5 / math.sqrt(d))
     np.testing.assert_allclose(o3, o0, atol=1e-12)
 
 
-def test_attention_rows_subset_matches_full():
+@pytest.mark.parametrize("attn", ATTN_IMPLS, ids=ATTN_IDS)
+def test_attention_rows_subset_matches_full(attn):
     rng = np.random.default_rng(6)
     g = oracle.MaskGeometry(4, 32, 1, 1, 0, 16, 16)
     q, k, v = _rand_qkv(rng, 1, 2, 128, 8)
-    o, lse = oracle.attention_ref(q, k, v, g)
+    o, lse = attn(q, k, v, g)
     rows = [0, 5, 31, 32, 77, 127]
-    os_, ls_ = oracle.attention_ref(q, k, v, g, rows=rows)
-    np.testing.assert_array_equal(os_, o[:, :, rows])
-    np.testing.assert_array_equal(ls_, lse[:, :, rows])
+    os_, ls_ = attn(q, k, v, g, rows=rows)
+    # (a subset changes only the matrix products' blocking: equal to rounding)
+    np.testing.assert_allclose(os_, o[:, :, rows], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(ls_, lse[:, :, rows], rtol=0, atol=1e-14)
 
 
 def test_shift_invariance_online_fixed_and_max():
@@ -426,6 +438,110 @@ def test_workload4_stressed_heads_fail_eligibility(config_inputs):
     assert np.any(gaps > 104.0)
 
 
+# ------------------------------------------------------------------ the fixed shift and the threshold
+# ("Unchaining the Softmax": each row starts from a bound on its logits; the
+# bound must sit at or above every live logit of the row, and eligibility is
+# "bound minus logit max <= 30 nats", decided per head)
+
+def _raw_live_row_max(q, k, g, scale):
+    """max over row i's live keys of the raw logit scale * q_i . k_j, by a loop
+    over rows with the live keys taken from row_mask (no mean, no bound)."""
+    B, H, N, d = q.shape
+    out = np.empty((B, H, N))
+    for i in range(N):
+        live = np.nonzero(oracle.row_mask(g, i))[0]
+        for b in range(B):
+            for h in range(H):
+                out[b, h, i] = max(scale * float(np.dot(q[b, h, i], k[b, h, j])) for j in live)
+    return out
+
+
+def _check_shift_audit(q, k, g):
+    """Both shift variants of each row: at least the row's largest raw live
+    logit (so no exponential exceeds 1 and none overflows), and at most the
+    head's gap estimate above it (so the largest term of an eligible head's
+    row is at least e^-30)."""
+    d = q.shape[-1]
+    scale = 1 / math.sqrt(d)
+    rec = oracle.head_bounds_ref(q, k, g)
+    rmax = _raw_live_row_max(q, k, g, scale)
+    for per_row in (False, True):
+        sh = oracle.row_shift_ref(q, rec, per_row=per_row)
+        assert np.all(sh >= rmax - 1e-12 * np.abs(rmax)), per_row
+        assert np.all(sh - rmax <= rec["gap_est"][:, :, None] + 1e-9), per_row
+
+
+SHIFT_GEOMS = [(5, 16, 1, 1, 0, 0, 0), (6, 16, 2, 0, 3, 0, 0), (4, 16, 0, 0, -1, 0, 0),
+               (5, 16, 1, 1, 2, 1, 0), (7, 16, 0, 0, 2, 0, 3), (3, 16, 2, 2, 0, 0, 0)]
+
+
+def test_row_shift_bounds_every_raw_live_logit():
+    """Exhaustive over every (row, live key) pair of small geometries whose keys
+    carry a large common offset (so q_i . mu_h is large and of either sign)."""
+    rng = np.random.default_rng(40)
+    for F, T, wb, wa, r, rg, nr in SHIFT_GEOMS:
+        g = oracle.MaskGeometry(F, T, wb, wa, r, 16, 16, rg, nr)
+        q, k, _ = _rand_qkv(rng, 2, 2, F * T, 8)
+        k = k + rng.standard_normal(8) * 6.0
+        _check_shift_audit(q, k, g)
+
+
+def test_row_shift_hand_values():
+    # the geometry of test_bounds_hand_example: keys 8 x (13, 14) and 8 x (7, 6),
+    # mean (10, 10), centred keys +-(3, 4) of norm 5; query row 3 is (6, 8) of
+    # norm 10, every other query is 0; scale 1/sqrt(2). bound = 10 * 5 / sqrt(2).
+    # Row 3: q . mu = 140, so both shifts are (50 + 140) / sqrt(2) = 190 / sqrt(2),
+    # which is its raw logit against (13, 14): 6 * 13 + 8 * 14 = 190. Zero rows:
+    # default shift = bound = 50 / sqrt(2), per-row shift = 0 (their logits are 0).
+    k = np.zeros((1, 1, 16, 2)); k[0, 0, :8] = (13, 14); k[0, 0, 8:] = (7, 6)
+    q = np.zeros((1, 1, 16, 2)); q[0, 0, 3] = (6, 8)
+    g = oracle.MaskGeometry(1, 16, 0, 0, -1, 16, 16)
+    rec = oracle.head_bounds_ref(q, k, g)
+    sq2 = math.sqrt(2)
+    sh = oracle.row_shift_ref(q, rec)
+    assert sh[0, 0, 3] == pytest.approx(190 / sq2)
+    assert np.allclose(np.delete(sh[0, 0], 3), 50 / sq2)
+    shr = oracle.row_shift_ref(q, rec, per_row=True)
+    assert shr[0, 0, 3] == pytest.approx(190 / sq2)
+    assert np.allclose(np.delete(shr[0, 0], 3), 0.0)
+    assert _raw_live_row_max(q, k, g, 1 / sq2)[0, 0, 3] == pytest.approx(190 / sq2)
+
+
+def _threshold_head(scale):
+    """One frame of 16 keys in d = 2: 8 x (5, 0) and 8 x (-5, 0), so mu = 0,
+    K_max = 5 and C_max = 0; query row 0 is (6, 0) (Q_max = 6), the rest 0.
+    gap_est = scale * 6 * 5 exactly (scale 255/256, 1, 257/256 give 29.8828125,
+    30 and 30.1171875, all exact in fp32 and fp64)."""
+    k = np.zeros((1, 1, 16, 2)); k[0, 0, :8, 0] = 5.0; k[0, 0, 8:, 0] = -5.0
+    q = np.zeros((1, 1, 16, 2)); q[0, 0, 0, 0] = 6.0
+    return q, k, oracle.MaskGeometry(1, 16, 0, 0, -1, 16, 16)
+
+
+THRESHOLD_CASES = [(255 / 256, 29.8828125, True), (1.0, 30.0, True), (257 / 256, 30.1171875, False)]
+
+
+def test_eligibility_threshold_is_30_nats_inclusive():
+    for scale, gap, elig in THRESHOLD_CASES:
+        q, k, g = _threshold_head(scale)
+        rec = oracle.head_bounds_ref(q, k, g, scale=scale)
+        assert rec["c_max"][0, 0] == 0.0 and rec["k_max"][0, 0] == 5.0 and rec["q_max"][0, 0] == 6.0
+        assert rec["gap_est"][0, 0] == gap
+        assert bool(rec["eligible"][0, 0]) is elig, (scale, gap)
+    assert oracle.GAP_THRESHOLD_NATS == 30.0
+
+
+def test_rope_tables_1d_hand_angle():
+    # d = 8, base 10^4: pair i of position n turns by n * 10^(-4 * 2i / 8) = n * 10^-i;
+    # position 3, pair 1: 0.3 rad; position 5, pair 2: 0.05 rad; position 0: 0
+    c, s = oracle.rope_tables_1d(6, 8)
+    assert c.shape == (6, 4)
+    assert c[3, 1] == pytest.approx(math.cos(0.3), abs=1e-15)
+    assert s[3, 1] == pytest.approx(math.sin(0.3), abs=1e-15)
+    assert s[5, 2] == pytest.approx(math.sin(0.05), abs=1e-15)
+    np.testing.assert_array_equal(c[0], 1.0)
+    np.testing.assert_array_equal(s[0], 0.0)
+
+
 def test_live_flops_closed_form():
     assert oracle.live_flops(_geom(workloads.workload(2).mask_tuple()), 1, 8, 128) == 4 * 128 * 8 * 117 * 960 * 960
     assert oracle.live_flops(_geom(workloads.workload(5).mask_tuple()), 1, 4, 128) == 2727346176000
@@ -453,17 +569,19 @@ def _run_pins_quietly(fns):
     return failed
 
 
-def test_planted_mistake_dropped_reference_frame_is_caught(monkeypatch):
+@pytest.mark.parametrize("attn", ATTN_IMPLS, ids=ATTN_IDS)
+def test_planted_mistake_dropped_reference_frame_is_caught(monkeypatch, attn):
     def no_ref_rows(g, rows):
         fr = np.arange(g.N) // g.T
         fi = (np.asarray(rows) // g.T)[:, None]
         return (fr[None, :] >= fi - g.wb) & (fr[None, :] <= fi + g.wa)
     monkeypatch.setattr(O, "mask_rows", no_ref_rows)
     assert _run_pins_quietly([test_plan_matches_hand_derived_golden,
-                              lambda: test_attention_matches_bruteforce_loops((3, 4, 1, 1, 0))]) == 2
+                              lambda: test_attention_matches_bruteforce_loops(attn, (3, 4, 1, 1, 0))]) == 2
 
 
-def test_planted_mistake_ignored_global_reference_queries_is_caught(monkeypatch):
+@pytest.mark.parametrize("attn", ATTN_IMPLS, ids=ATTN_IDS)
+def test_planted_mistake_ignored_global_reference_queries_is_caught(monkeypatch, attn):
     def keys_only_rows(g, rows):
         fr = np.arange(g.N) // g.T
         fi = (np.asarray(rows) // g.T)[:, None]
@@ -473,10 +591,11 @@ def test_planted_mistake_ignored_global_reference_queries_is_caught(monkeypatch)
         return m
     monkeypatch.setattr(O, "mask_rows", keys_only_rows)
     assert _run_pins_quietly([test_plan_matches_hand_derived_golden,
-                              lambda: test_attention_matches_bruteforce_loops((4, 3, 0, 0, 2, 1))]) == 2
+                              lambda: test_attention_matches_bruteforce_loops(attn, (4, 3, 0, 0, 2, 1))]) == 2
 
 
-def test_planted_mistake_single_reference_frame_is_caught(monkeypatch):
+@pytest.mark.parametrize("attn", ATTN_IMPLS, ids=ATTN_IDS)
+def test_planted_mistake_single_reference_frame_is_caught(monkeypatch, attn):
     def first_ref_only_rows(g, rows):
         fr = np.arange(g.N) // g.T
         fi = (np.asarray(rows) // g.T)[:, None]
@@ -488,10 +607,11 @@ def test_planted_mistake_single_reference_frame_is_caught(monkeypatch):
         return m
     monkeypatch.setattr(O, "mask_rows", first_ref_only_rows)
     assert _run_pins_quietly([test_plan_matches_hand_derived_golden,
-                              lambda: test_attention_matches_bruteforce_loops((6, 2, 0, 0, 1, 0, 3))]) == 2
+                              lambda: test_attention_matches_bruteforce_loops(attn, (6, 2, 0, 0, 1, 0, 3))]) == 2
 
 
-def test_planted_mistake_exclusive_window_is_caught(monkeypatch):
+@pytest.mark.parametrize("attn", ATTN_IMPLS, ids=ATTN_IDS)
+def test_planted_mistake_exclusive_window_is_caught(monkeypatch, attn):
     def excl_rows(g, rows):
         fr = np.arange(g.N) // g.T
         fi = (np.asarray(rows) // g.T)[:, None]
@@ -501,7 +621,7 @@ def test_planted_mistake_exclusive_window_is_caught(monkeypatch):
         return m
     monkeypatch.setattr(O, "mask_rows", excl_rows)
     assert _run_pins_quietly([test_plan_matches_hand_derived_golden,
-                              lambda: test_attention_matches_bruteforce_loops((3, 4, 1, 1, 0))]) == 2
+                              lambda: test_attention_matches_bruteforce_loops(attn, (3, 4, 1, 1, 0))]) == 2
 
 
 def test_planted_mistake_uncentred_bound_is_caught(monkeypatch):
@@ -518,24 +638,20 @@ def test_planted_mistake_uncentred_bound_is_caught(monkeypatch):
     assert _run_pins_quietly([test_bounds_hand_example, test_bounds_translation_invariance]) == 2
 
 
-def test_planted_mistake_transposed_operand_is_caught(monkeypatch):
-    real = O.attention_ref
-
-    def swapped(q, k, v, g, scale=None, rows=None, chunk=256):
-        return real(q, v, k, g, scale, rows, chunk)            # K and V exchanged
-    monkeypatch.setattr(oracle, "attention_ref", swapped)
-    assert _run_pins_quietly([lambda: test_attention_matches_bruteforce_loops((3, 4, 1, 1, 0)),
-                              test_attention_dense_matches_torch_sdpa]) == 2
+@pytest.mark.parametrize("real", ATTN_IMPLS, ids=ATTN_IDS)
+def test_planted_mistake_transposed_operand_is_caught(real):
+    def swapped(q, k, v, g, scale=None, rows=None):
+        return real(q, v, k, g, scale, rows)            # K and V exchanged
+    assert _run_pins_quietly([lambda: test_attention_matches_bruteforce_loops(swapped, (3, 4, 1, 1, 0)),
+                              lambda: test_attention_dense_matches_torch_sdpa(swapped)]) == 2
 
 
-def test_planted_mistake_missing_scale_is_caught(monkeypatch):
-    real = O.attention_ref
-
-    def unscaled(q, k, v, g, scale=None, rows=None, chunk=256):
-        return real(q, k, v, g, 1.0, rows, chunk)
-    monkeypatch.setattr(oracle, "attention_ref", unscaled)
-    assert _run_pins_quietly([lambda: test_attention_matches_bruteforce_loops((3, 4, 1, 1, 0)),
-                              test_attention_dense_matches_torch_sdpa]) == 2
+@pytest.mark.parametrize("real", ATTN_IMPLS, ids=ATTN_IDS)
+def test_planted_mistake_missing_scale_is_caught(real):
+    def unscaled(q, k, v, g, scale=None, rows=None):
+        return real(q, k, v, g, 1.0, rows)
+    assert _run_pins_quietly([lambda: test_attention_matches_bruteforce_loops(unscaled, (3, 4, 1, 1, 0)),
+                              lambda: test_attention_dense_matches_torch_sdpa(unscaled)]) == 2
 
 
 # ------------------------------------------------------------------ producer (norm + rotary + layout)
@@ -650,3 +766,57 @@ def test_planted_mistake_norm_without_eps_or_gamma_is_caught(monkeypatch):
     for bad in (no_eps, no_gamma):
         monkeypatch.setattr(oracle, "rms_norm_ref", bad)
         assert _run_pins_quietly([test_rms_norm_matches_torch_and_closed_forms]) == 1
+
+
+def test_planted_mistake_shift_without_mean_term_is_caught(monkeypatch):
+    real = oracle.row_shift_ref
+
+    def no_qmu(q, rec, scale=None, per_row=False, k_max=None):
+        zero = dict(rec, mu=np.zeros_like(rec["mu"]))
+        return real(q, zero, scale=scale, per_row=per_row, k_max=k_max)
+    monkeypatch.setattr(oracle, "row_shift_ref", no_qmu)
+    assert _run_pins_quietly([test_row_shift_bounds_every_raw_live_logit, test_row_shift_hand_values]) == 2
+
+
+def test_planted_mistake_shift_without_scale_on_mean_term_is_caught(monkeypatch):
+    def unscaled_qmu(q, rec, scale=None, per_row=False, k_max=None):
+        q = np.asarray(q, np.float64)
+        scale = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
+        qmu = np.einsum("bhnd,bhd->bhn", q, rec["mu"])
+        if per_row:
+            return scale * np.sqrt((q * q).sum(-1)) * rec["k_max"][:, :, None] + qmu
+        return rec["bound"][:, :, None] + qmu
+    monkeypatch.setattr(oracle, "row_shift_ref", unscaled_qmu)
+    assert _run_pins_quietly([test_row_shift_bounds_every_raw_live_logit, test_row_shift_hand_values]) == 2
+
+
+def test_planted_mistake_shift_without_scale_is_caught(monkeypatch):
+    real = oracle.row_shift_ref
+
+    def unscaled(q, rec, scale=None, per_row=False, k_max=None):
+        q = np.asarray(q, np.float64)
+        s = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
+        return real(q, rec, scale=s, per_row=per_row, k_max=k_max) / s
+    monkeypatch.setattr(oracle, "row_shift_ref", unscaled)
+    assert _run_pins_quietly([test_row_shift_hand_values]) == 1
+
+
+@pytest.mark.parametrize("mistake", ["exclusive", "threshold25", "threshold100"])
+def test_planted_mistake_threshold_is_caught(monkeypatch, mistake):
+    real = oracle.head_bounds_ref
+
+    def bad(q, k, g, scale=None, threshold=oracle.GAP_THRESHOLD_NATS):
+        if mistake == "threshold25":
+            return real(q, k, g, scale=scale, threshold=25.0)
+        if mistake == "threshold100":
+            return real(q, k, g, scale=scale, threshold=100.0)
+        rec = real(q, k, g, scale=scale, threshold=threshold)
+        return dict(rec, eligible=rec["gap_est"] < threshold)
+    monkeypatch.setattr(oracle, "head_bounds_ref", bad)
+    assert _run_pins_quietly([test_eligibility_threshold_is_30_nats_inclusive]) == 1
+
+
+def test_planted_mistake_rope_base_is_caught(monkeypatch):
+    real = oracle.rope_tables_1d
+    monkeypatch.setattr(oracle, "rope_tables_1d", lambda n, d, base=10000.0: real(n, d, base=1000.0))
+    assert _run_pins_quietly([test_rope_tables_1d_hand_angle]) == 1
