@@ -203,10 +203,23 @@ def mask_variant_timing(w, qd, kd, vd, reps: int = 10):
     return out
 
 
-def flush_llc(buf):
-    """Write the whole scratch buffer (512 MiB, twice the last-level cache),
-    so the next kernel's inputs come from HBM."""
-    buf.fill_(0x5A)
+def flush_llc(bufs):
+    """Evict the last-level cache (256 MB) before a timed launch: write one
+    512 MiB scratch buffer, then read another 512 MiB one (a sum), so that
+    the cache ends up holding clean lines of the second buffer and the
+    timed kernel neither hits its own inputs nor pays for writing back the
+    flush's data."""
+    import torch
+    wbuf, rbuf, sink = bufs
+    wbuf.fill_(0x5A)
+    torch.sum(rbuf, dim=0, out=sink)
+
+
+def make_flush_buffers(dev):
+    import torch
+    return (torch.empty(512 << 20, dtype=torch.uint8, device=dev),
+            torch.ones((512 << 20) // 4, dtype=torch.float32, device=dev),
+            torch.zeros((), dtype=torch.float32, device=dev))
 
 
 def producer_timing(w, dev, bounds_ms: float, flush_buf, reps: int = 20):
@@ -412,6 +425,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="only the timed steps (for profiling runs): no comparator, producer, mask variants, "
                          "extra workloads or oracle check")
+    ap.add_argument("--only", choices=["bounds", "producer"], default=None,
+                    help="profiling runs: only the flushed bounds (or producer) repetitions on the workload, "
+                         "then a one-line JSON of that record")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device-to-device copy of 512 MiB three times (the known-size "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -444,12 +460,18 @@ def main():
     fs.lib()
     w = workloads.workload(args.workload)
     print(f"[bench] workload {args.workload} {w.name}: generating inputs", file=sys.stderr, flush=True)
+    flush_buf = make_flush_buffers(dev)
+    if args.only == "producer":
+        print(json.dumps({"workload": w.name, "producer": producer_timing(w, dev, 0.0, flush_buf)}), flush=True)
+        return
     q, k, v = workloads.make_inputs(w, seed=0)
     td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     qd, kd, vd = (torch.from_numpy(x).to(td).to(dev) for x in (q, k, v))
-    od = torch.empty_like(qd)
-    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     mask = F.to_mask(w)
+    if args.only == "bounds":
+        print(json.dumps({"workload": w.name, "bounds": bounds_timing(w, qd, kd, mask, flush_buf)}), flush=True)
+        return
+    od = torch.empty_like(qd)
     nqb, nnz = fs.plan_size(mask)
     flags = fs.make_flags(args.mode, waves=args.waves, rows_per_wave=args.rows, key_step=args.kstep, ring=args.ring)
     waves, rows_pw, kstep, wgs, lds = fs.launch_info(tuple(qd.shape), fs.BF16 if w.dtype == "bf16" else fs.F32,
