@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
 
+#include <mutex>
+
 #include "fsattn_internal.h"
 
 namespace fsattn {
@@ -395,6 +397,32 @@ hipError_t launch_all(const BoundsParams &p, hipStream_t st, const ProduceParams
 }
 
 }  // namespace
+
+// Workspace of fsattn_head_bounds_noalloc: one array per device, held from
+// the time the library's code object is loaded until the process ends. The
+// bounds kernels overwrite every partial result they later read, so nothing
+// in it has to start at zero. In host code its name only stands for the
+// symbol: the device address comes from hipGetSymbolAddress, once per
+// device (each device holds its own copy at its own address).
+static __device__ __align__(256) unsigned char scratch[kBoundsScratchBytes];
+
+hipError_t bounds_scratch(void **ptr) {
+  static std::mutex mu;
+  static void *addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_head_bounds(const BoundsParams &p, int dtype, hipStream_t st) {
   if (dtype == FSATTN_BF16) {

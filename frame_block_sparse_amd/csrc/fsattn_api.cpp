@@ -140,6 +140,29 @@ extern "C" fsattn_status fsattn_head_bounds(void *hip_stream, const fsattn_shape
   return e == hipSuccess ? FSATTN_OK : FSATTN_ERR_HIP;
 }
 
+extern "C" fsattn_status fsattn_head_bounds_noalloc(void *hip_stream, const fsattn_shape *s,
+                                                    const fsattn_mask *m, fsattn_tensor q, fsattn_tensor k,
+                                                    float scale, float gap_threshold_nats, float *key_mean,
+                                                    fsattn_head_bound *rec) {
+  fsattn_status st = check_shape(s, m);
+  if (st != FSATTN_OK) return st;
+  const int esz = elem_size(s->dtype);
+  if ((st = check_tensor(q, esz, s->head_dim)) != FSATTN_OK) return st;
+  if ((st = check_tensor(k, esz, s->head_dim)) != FSATTN_OK) return st;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return FSATTN_ERR_INVALID_ARGUMENT;
+  if (!(gap_threshold_nats >= 0.f)) return FSATTN_ERR_INVALID_ARGUMENT;
+  if (!key_mean || !rec) return FSATTN_ERR_INVALID_ARGUMENT;
+  const WsLayout w = ws_layout(s, m);
+  if (w.total > kBoundsScratchBytes) return FSATTN_ERR_BUFFER_TOO_SMALL;
+  void *scratch = nullptr;
+  if (bounds_scratch(&scratch) != hipSuccess) return FSATTN_ERR_HIP;
+  const BoundsParams p = bounds_params(s, m, q, k, scale, gap_threshold_nats, key_mean, rec, scratch, w);
+  const hipError_t e = launch_head_bounds(p, s->dtype, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? FSATTN_OK : FSATTN_ERR_HIP;
+}
+
+extern "C" size_t fsattn_head_bounds_noalloc_max_workspace(void) { return kBoundsScratchBytes; }
+
 extern "C" fsattn_status fsattn_produce(void *hip_stream, const fsattn_shape *s, const fsattn_mask *m,
                                         fsattn_tensor q_in, fsattn_tensor k_in, fsattn_tensor v_in,
                                         const float *gamma_q, const float *gamma_k, float eps,

@@ -83,6 +83,12 @@ struct BoundsParams {
 
 hipError_t launch_head_bounds(const BoundsParams &p, int dtype, hipStream_t st);
 
+// The device-resident workspace of fsattn_head_bounds_noalloc: its size,
+// and its address on the current device (bounds_kernels.hip).
+constexpr size_t kBoundsScratchBytes = size_t(4) << 20;
+constexpr int kMaxDevices = 64;
+hipError_t bounds_scratch(void **ptr);
+
 // The input-producing chain fused into the bounds' first pass
 // (fsattn_produce): Q, K and V are read through the input views, Q and K are
 // RMS-normalised (gamma [H][d], when given) and rotated (angle tables

@@ -82,6 +82,11 @@ def lib() -> ctypes.CDLL:
     L.fsattn_head_bounds.argtypes = [ctypes.c_void_p, ctypes.POINTER(Shape), ctypes.POINTER(Mask), Tensor, Tensor,
                                      ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_size_t]
+    L.fsattn_head_bounds_noalloc.argtypes = [ctypes.c_void_p, ctypes.POINTER(Shape), ctypes.POINTER(Mask), Tensor,
+                                             Tensor, ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
+                                             ctypes.c_void_p]
+    L.fsattn_head_bounds_noalloc_max_workspace.argtypes = []
+    L.fsattn_head_bounds_noalloc_max_workspace.restype = ctypes.c_size_t
     L.fsattn_produce.argtypes = [ctypes.c_void_p, ctypes.POINTER(Shape), ctypes.POINTER(Mask), Tensor, Tensor,
                                  Tensor, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
                                  ctypes.c_void_p, Tensor, Tensor, Tensor, ctypes.c_float, ctypes.c_float,
@@ -104,7 +109,8 @@ def lib() -> ctypes.CDLL:
     if L.fsattn_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{LIB_PATH} has ABI {L.fsattn_abi_version()}, the binding expects {ABI_VERSION}: "
                            "rebuild it")
-    for name in ("fsattn_plan_size", "fsattn_plan", "fsattn_plan_device", "fsattn_head_bounds", "fsattn_produce",
+    for name in ("fsattn_plan_size", "fsattn_plan", "fsattn_plan_device", "fsattn_head_bounds",
+                 "fsattn_head_bounds_noalloc", "fsattn_produce",
                  "fsattn_forward",
                  "fsattn_forward_launch_info", "fsattn_mfma_probe", "fsattn_prior_art_forward"):
         getattr(L, name).restype = ctypes.c_int
@@ -270,6 +276,29 @@ def head_bounds(q: torch.Tensor, k: torch.Tensor, mask, scale: Optional[float] =
                                 float(scale), float(threshold), out.key_mean.data_ptr(), out.rec.data_ptr(),
                                 workspace.data_ptr(), workspace.numel()), "fsattn_head_bounds")
     return out
+
+
+def head_bounds_noalloc(q: torch.Tensor, k: torch.Tensor, mask, scale: Optional[float] = None,
+                        threshold: float = DEFAULT_GAP_NATS, out: Optional[Bounds] = None) -> Bounds:
+    """fsattn_head_bounds_noalloc: the same records with the library's
+    device-resident workspace (no workspace argument; the outputs are still
+    the caller's)."""
+    m = to_mask(mask)
+    s = _shape(q)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = Bounds(torch.empty((B, H, d), dtype=torch.float32, device=q.device),
+                     torch.empty((B, H, 8), dtype=torch.float32, device=q.device))
+    _check(lib().fsattn_head_bounds_noalloc(_stream(q), ctypes.byref(s), ctypes.byref(m), _tensor(q), _tensor(k),
+                                            float(scale), float(threshold), out.key_mean.data_ptr(),
+                                            out.rec.data_ptr()), "fsattn_head_bounds_noalloc")
+    return out
+
+
+def noalloc_max_workspace() -> int:
+    return lib().fsattn_head_bounds_noalloc_max_workspace()
 
 
 def _f32_ptr(t: Optional[torch.Tensor], shape, what: str) -> int:

@@ -214,6 +214,30 @@ fsattn_status fsattn_head_bounds(void *hip_stream, const fsattn_shape *s, const 
                                  fsattn_head_bound *rec, void *workspace, size_t workspace_bytes);
 
 /*
+ * fsattn_head_bounds without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same kernels and the same
+ * results, bit for bit, with the workspace in a device-resident array of
+ * fsattn_head_bounds_noalloc_max_workspace() bytes (4 MiB) that the library
+ * holds on each device it runs on until the process ends. Calls no
+ * allocating routine. Arguments and errors are those of fsattn_head_bounds,
+ * plus BUFFER_TOO_SMALL when fsattn_head_bounds_workspace_bytes() for the
+ * shape exceeds that size (e.g. B*H = 16 at 16 frames of 1024 tokens and
+ * head_dim 128 needs about 1.2 MiB). Every call on a device shares that
+ * device's array, and nothing in it needs to start at zero: calls that
+ * overlap on one device (concurrent streams, or threads) race and must be
+ * serialised by the caller. The first call on a device looks up the
+ * array's address there (FSATTN_ERR_HIP on failure).
+ */
+fsattn_status fsattn_head_bounds_noalloc(void *hip_stream, const fsattn_shape *s, const fsattn_mask *m,
+                                         fsattn_tensor q, fsattn_tensor k, float scale, float gap_threshold_nats,
+                                         float *key_mean, fsattn_head_bound *rec);
+
+/* Size in bytes of the device-resident workspace of
+ * fsattn_head_bounds_noalloc (the largest workspace it accepts). */
+size_t fsattn_head_bounds_noalloc_max_workspace(void);
+
+/*
  * The input-producing chain fused with the bounds ("Layout Is the ABI",
  * Fig. 5: the small operations that make attention's inputs run as one
  * kernel that writes its consumer's layout). Reads Q, K and V through the

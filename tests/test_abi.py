@@ -146,6 +146,28 @@ def test_head_bounds_validation():
     assert _bounds_call(wsb=16) == 4
 
 
+def test_noalloc_bounds_validates_on_host():
+    """The allocation-free bounds entry rejects bad arguments and shapes whose
+    workspace exceeds its device-resident array before any HIP call."""
+    L = fs.lib()
+    assert L.fsattn_head_bounds_noalloc_max_workspace() == 4 << 20
+    m = F.to_mask((16, 1024, 15, 15, 0, 64, 64))
+    big = F.Shape(1, 64, 16 * 1024, 128, 1)
+    assert L.fsattn_head_bounds_workspace_bytes(ctypes.byref(big), ctypes.byref(m)) > 4 << 20
+    ok = F.Shape(1, 8, 16 * 1024, 128, 1)
+    assert L.fsattn_head_bounds_workspace_bytes(ctypes.byref(ok), ctypes.byref(m)) <= 4 << 20
+
+    def call(shape, km=FAKE, rec=FAKE, scale=0.125, mask=m):
+        t = _t(n=16 * 1024, d=128, h=64)
+        return L.fsattn_head_bounds_noalloc(None, ctypes.byref(shape), ctypes.byref(mask), t, t, scale, 30.0, km, rec)
+    assert call(big) == 4                                   # beyond the array
+    assert call(ok, km=None) == 1
+    assert call(ok, rec=None) == 1
+    assert call(ok, scale=-1.0) == 1
+    assert call(F.Shape(1, 8, 16 * 1024, 96, 1)) == 3       # head_dim not built
+    assert call(ok, mask=F.to_mask((16, 1024, 15, 15, 0, 48, 64))) == 2
+
+
 def test_workspace_bytes():
     L = fs.lib()
     s = F.Shape(1, 4, 48960, 128, 1)
