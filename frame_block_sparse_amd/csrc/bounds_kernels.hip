@@ -113,11 +113,19 @@ __device__ inline float block_max(float v, float *sh) {
   return r;
 }
 
-// sum_{i < n} x[i * stride], added in index order, with up to 8 loads in
-// flight (the order of the additions is the plain sequential one).
+// sum_{i < n} x[i * stride], added in index order, with up to 32 loads in
+// flight (the order of the additions is the plain sequential one; a frame
+// of 8160 tokens has 32 chunk sums, which then cost one round trip).
 __device__ inline float ordered_sum(const float *x, int n, int64_t stride) {
   float s = 0.f;
   int i = 0;
+  for (; i + 32 <= n; i += 32) {
+    float v[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) v[e] = x[(int64_t)(i + e) * stride];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) s += v[e];
+  }
   for (; i + 8 <= n; i += 8) {
     float v[8];
 #pragma unroll
