@@ -26,6 +26,7 @@ import hashlib
 import json
 import math
 import os
+import socket
 import sys
 import time
 
@@ -545,6 +546,7 @@ def main():
         "data": "synthetic",
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "prewarm_s": args.prewarm_seconds,
+        "host": socket.gethostname(),
         "config": {
             "workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
             "head_dim": w.head_dim, "frames": w.num_frames, "tokens_per_frame": w.tokens_per_frame,
