@@ -120,8 +120,7 @@ __device__ inline float add_bf16_pair(float acc, unsigned x) {
 // Issued from inline assembly so that the compiler's wait insertion, which
 // cannot tell the two staging buffers apart, does not stall every LDS read
 // behind the in-flight prefetch; completion is awaited explicitly
-// (wait_vmem() before the step barrier). M0 carries the LDS base; no
-// other code in these kernels uses M0.
+// (wait_vmem() before the step barrier). M0 carries the LDS base.
 // The address is a wave-uniform 64-bit base (SGPR pair) plus a 32-bit
 // per-lane byte offset.
 __device__ inline uint64_t uniform_u64(uint64_t a) {
@@ -131,11 +130,12 @@ __device__ inline uint64_t uniform_u64(uint64_t a) {
 }
 __device__ inline uint64_t uniform_ptr(const void *p) { return uniform_u64(reinterpret_cast<uint64_t>(p)); }
 // (the scalar operands pass through readfirstlane, which only states what
-// they already are: wave-uniform)
+// they already are: wave-uniform; M0 is declared clobbered, so the compiler
+// keeps no value of its own in it across the copy)
 __device__ inline void dma16(uint64_t base, unsigned off, unsigned lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(uniform_u64(base)),
                "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory");
+               : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(0) through the builtin, which the compiler's own wait
