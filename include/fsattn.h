@@ -160,10 +160,13 @@ enum {
 #define FSATTN_DEFAULT_GAP_NATS 30.0f
 
 /*
- * Plan size: number of query blocks (seq_len / block_q) and number of live
- * (query block, key block) pairs, nnz = sum_f |L(f)| * (T/block_q) *
- * (T/block_k). Host only. Errors: INVALID_ARGUMENT (null pointer),
- * BLOCK_GEOMETRY.
+ * Plan size ("Deleting the Mask", Fig. 3: with blocks that divide the frame
+ * span, each query frame's live key blocks are whole frames of blocks):
+ * number of query blocks (seq_len / block_q) and number of live (query
+ * block, key block) pairs, nnz = sum_f |L(f)| * (T/block_q) * (T/block_k),
+ * where L(f) is the set of frames query frame f sees. Sizes the arrays of
+ * fsattn_plan / fsattn_plan_device. Host only. Errors: INVALID_ARGUMENT
+ * (null pointer), BLOCK_GEOMETRY.
  */
 fsattn_status fsattn_plan_size(const fsattn_mask *m, int64_t *num_q_blocks, int64_t *nnz);
 
@@ -192,8 +195,10 @@ fsattn_status fsattn_plan(const fsattn_mask *m, int32_t *row_ptr, int64_t row_pt
 fsattn_status fsattn_plan_device(void *hip_stream, const fsattn_mask *m, int32_t *row_ptr,
                                  int64_t row_ptr_len, int32_t *col_idx, int64_t col_idx_len);
 
-/* Bytes of device workspace fsattn_head_bounds needs for this shape and
- * mask; 0 if the arguments are invalid. */
+/* Bytes of device workspace fsattn_head_bounds (and fsattn_produce) needs
+ * for this shape and mask ("Unchaining the Softmax": the per-chunk partial
+ * key sums and norm maxima from which the per-head mean, norm maxima and
+ * window term are reduced); 0 if the arguments are invalid. */
 size_t fsattn_head_bounds_workspace_bytes(const fsattn_shape *s, const fsattn_mask *m);
 
 /*
