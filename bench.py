@@ -8,7 +8,8 @@ Inputs are resident in HBM before timing starts. The metric counts live-block
 FLOPs only: 4 * d per live (query, key) pair (QK^T and PV), summed over
 every head. The default workload is the largest single-GPU one (6 frames x
 8160 tokens, 4 heads, d = 128, bf16); workloads 2 and 3 are measured in the
-same run with the same protocol and reported under "workloads".
+same run with the same protocol and reported under "workloads", as is
+workload 4 (16 frames x 1024 tokens, dense, two heads that fail eligibility).
 
 Prints ONE JSON line. The roofline object describes the dominant kernel
 (the forward) from HIP events recorded around each of its launches on the
@@ -410,7 +411,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=5,
                     help="1..5 (default 5: bf16, 6 frames x 8160 tokens, the largest single-GPU workload)")
-    ap.add_argument("--extra-workloads", default="2,3",
+    ap.add_argument("--extra-workloads", default="2,3,4",
                     help="comma-separated workloads also measured (forward median/min, flushed bounds, error); "
                          "empty for none")
     ap.add_argument("--waves", type=int, default=0)
@@ -547,6 +548,7 @@ def main():
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "prewarm_s": args.prewarm_seconds,
         "host": socket.gethostname(),
+        "device_uuid": str(getattr(torch.cuda.get_device_properties(dev), "uuid", "")),
         "config": {
             "workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
             "head_dim": w.head_dim, "frames": w.num_frames, "tokens_per_frame": w.tokens_per_frame,

@@ -6,11 +6,15 @@
 // [f - window_before, f + window_after] plus the reference frames (all
 // frames for the queries of global reference frames), so every
 // query block of frame f lists the same key blocks: those of its live
-// frames, ascending. One workgroup per query frame finds where the frame's
-// rows start (the sum of the earlier frames' row lengths), then writes its
-// row_ptr entries and its col_idx rows with consecutive threads on
-// consecutive entries.
+// frames, ascending. The query blocks of a frame are split over several
+// workgroups (blockIdx.y); each finds where the frame's rows start (the sum
+// of the earlier frames' row lengths), writes the row_ptr entries of its
+// query blocks, and writes their col_idx rows: a thread computes the
+// column of row entry e once and stores it into every row of its slice,
+// consecutive threads on consecutive entries.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 
 #include "fsattn_internal.h"
 
@@ -22,6 +26,7 @@ constexpr int kPlanThreads = 256;
 struct PlanGeom {
   LiveGeom live;
   int qpf, kpf;
+  int qb_per_wg;   // query blocks per workgroup
 };
 
 // Number of frames in the live intervals of query frame f.
@@ -35,6 +40,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanGeom g, int32_t 
   __shared__ int64_t part[kPlanThreads];
   const int f = blockIdx.x;
   const int t = threadIdx.x;
+  // this workgroup's query blocks of frame f
+  const int q0 = blockIdx.y * g.qb_per_wg, q1 = min(g.qpf, q0 + g.qb_per_wg);
   // entries before frame f: its predecessors' live-frame counts times the
   // blocks per frame pair
   int64_t before = 0;
@@ -52,15 +59,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanGeom g, int32_t 
   int iv[4], first;
   const int n = live_count(g.live, f, iv, &first);
   const int E = n * g.kpf;   // entries per query block of this frame
-  if (f == 0 && t == 0) row_ptr[0] = 0;
-  for (int i = t; i < g.qpf; i += kPlanThreads)
+  if (f == 0 && q0 == 0 && t == 0) row_ptr[0] = 0;
+  for (int i = q0 + t; i < q1; i += kPlanThreads)
     row_ptr[(int64_t)f * g.qpf + i + 1] = (int32_t)(base + (int64_t)(i + 1) * E);
-  const int64_t total = (int64_t)g.qpf * E;
-  for (int64_t idx = t; idx < total; idx += kPlanThreads) {
-    const int e = (int)(idx % E);
+  for (int e = t; e < E; e += kPlanThreads) {
     const int j = e / g.kpf, c = e % g.kpf;   // j-th live frame, its c-th key block
     const int frame = j < first ? iv[0] + j : iv[2] + (j - first);
-    col_idx[base + idx] = frame * g.kpf + c;
+    const int32_t col = frame * g.kpf + c;
+    for (int i = q0; i < q1; ++i) col_idx[base + (int64_t)i * E + e] = col;
   }
 }
 
@@ -71,7 +77,11 @@ hipError_t launch_plan_device(const fsattn_mask &m, int32_t *row_ptr, int32_t *c
   g.live = live_geom(m);
   g.qpf = m.tokens_per_frame / m.block_q;
   g.kpf = m.tokens_per_frame / m.block_k;
-  hipLaunchKernelGGL(plan_kernel, dim3(g.live.F), dim3(kPlanThreads), 0, st, g, row_ptr, col_idx);
+  // about 256 workgroups in all (the frames' query blocks split evenly)
+  const int slices = std::max(1, std::min(g.qpf, (256 + g.live.F - 1) / g.live.F));
+  g.qb_per_wg = (g.qpf + slices - 1) / slices;
+  const int ny = (g.qpf + g.qb_per_wg - 1) / g.qb_per_wg;
+  hipLaunchKernelGGL(plan_kernel, dim3(g.live.F, ny), dim3(kPlanThreads), 0, st, g, row_ptr, col_idx);
   return hipGetLastError();
 }
 

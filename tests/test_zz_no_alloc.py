@@ -1,7 +1,9 @@
 """fsattn_head_bounds_noalloc (the bounds with the library's device-resident
 workspace) against fsattn_head_bounds with a caller workspace, through the
 C ABI: bit-equal records and key means on two calls in a row, the second on
-a smaller input, with no change in the device's free memory."""
+a smaller input, with no change in the device's free memory; and the same
+call captured in a HIP graph (the use it exists for), replayed on new
+inputs."""
 import numpy as np
 import pytest
 import torch
@@ -70,3 +72,33 @@ def test_noalloc_rejects_shapes_beyond_its_workspace():
     with pytest.raises(fs.FsattnError) as e:
         fs.head_bounds_noalloc(q, q, w)
     assert e.value.status == 4
+
+
+def test_noalloc_bounds_in_a_captured_graph():
+    """Captured once, replayed three times: before each replay the static
+    inputs are overwritten eagerly (and the device synchronised); every
+    replay's records equal the eager workspace entry's on the same inputs."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    dev = torch.device("cuda:0")
+    w = workloads.make_workload("graph", 1, 4, 6, 480, 128, "bf16", 1, 1, 0, 48, 80)
+    sets = [_inputs(w, dev, seed) for seed in (11, 12, 13, 14)]
+    qs, ks = (t.clone() for t in sets[0])
+    out = fs.head_bounds_noalloc(qs, ks, w)          # warm (address lookup) and the output buffers
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fs.head_bounds_noalloc(qs, ks, w, out=out)
+    torch.cuda.synchronize()
+    for rep, (q, k) in enumerate(sets[1:]):
+        _say(f"[noalloc-graph] replay {rep}")
+        qs.copy_(q)
+        ks.copy_(k)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = fs.head_bounds(q, k, w)
+        torch.cuda.synchronize()
+        assert torch.equal(out.rec, ref.rec), rep
+        assert torch.equal(out.key_mean, ref.key_mean), rep
+
