@@ -178,6 +178,45 @@ def _stream(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+# Host-side checks of what the C ABI cannot see (the extent, dtype and
+# device of each buffer): a mismatch would otherwise make a kernel read or
+# write outside a buffer. Shapes and dtypes are checked first, then that
+# every tensor is on the first operand's GPU.
+
+def _same_operands(what: str, ref: torch.Tensor, *ts: torch.Tensor):
+    if ref.dim() != 4:
+        raise FsattnError(1, f"{what}: tensors must be [B, H, N, d], got shape {tuple(ref.shape)}")
+    for t in ts:
+        if tuple(t.shape) != tuple(ref.shape):
+            raise FsattnError(1, f"{what}: operand of shape {tuple(t.shape)} beside {tuple(ref.shape)}")
+        if t.dtype != ref.dtype:
+            raise FsattnError(1, f"{what}: operand of dtype {t.dtype} beside {ref.dtype}")
+
+
+def _f32_buffer(what: str, t: torch.Tensor, numel: int):
+    if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() < numel:
+        raise FsattnError(1, f"{what} must be a contiguous float32 tensor of at least {numel} elements")
+
+
+def _bounds_buffers(what: str, b: "Bounds", B: int, H: int, d: int):
+    _f32_buffer(f"{what}: key_mean", b.key_mean, B * H * d)
+    _f32_buffer(f"{what}: rec", b.rec, B * H * 8)
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    if not t.is_contiguous():
+        raise FsattnError(1, "a workspace must be contiguous")
+    return t.numel() * t.element_size()
+
+
+def _on_gpu(what: str, ref: torch.Tensor, *ts: Optional[torch.Tensor]):
+    if not ref.is_cuda:
+        raise FsattnError(1, f"{what}: tensors must be on a GPU, got {ref.device}")
+    for t in ts:
+        if t is not None and t.device != ref.device:
+            raise FsattnError(1, f"{what}: tensors on {t.device} and {ref.device}")
+
+
 # ----------------------------------------------------------------- plan
 
 def plan_size(mask) -> Tuple[int, int]:
@@ -261,10 +300,14 @@ def head_bounds(q: torch.Tensor, k: torch.Tensor, mask, scale: Optional[float] =
                 threshold: float = DEFAULT_GAP_NATS, workspace: Optional[torch.Tensor] = None,
                 out: Optional[Bounds] = None) -> Bounds:
     m = to_mask(mask)
+    _same_operands("fsattn_head_bounds", q, k)
     s = _shape(q)
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if out is not None:
+        _bounds_buffers("fsattn_head_bounds", out, B, H, d)
+    _on_gpu("fsattn_head_bounds", q, k, workspace, *((out.key_mean, out.rec) if out is not None else ()))
     L = lib()
     need = L.fsattn_head_bounds_workspace_bytes(ctypes.byref(s), ctypes.byref(m))
     if workspace is None:
@@ -274,7 +317,7 @@ def head_bounds(q: torch.Tensor, k: torch.Tensor, mask, scale: Optional[float] =
                      torch.empty((B, H, 8), dtype=torch.float32, device=q.device))
     _check(L.fsattn_head_bounds(_stream(q), ctypes.byref(s), ctypes.byref(m), _tensor(q), _tensor(k),
                                 float(scale), float(threshold), out.key_mean.data_ptr(), out.rec.data_ptr(),
-                                workspace.data_ptr(), workspace.numel()), "fsattn_head_bounds")
+                                workspace.data_ptr(), _nbytes(workspace)), "fsattn_head_bounds")
     return out
 
 
@@ -284,10 +327,14 @@ def head_bounds_noalloc(q: torch.Tensor, k: torch.Tensor, mask, scale: Optional[
     device-resident workspace (no workspace argument; the outputs are still
     the caller's)."""
     m = to_mask(mask)
+    _same_operands("fsattn_head_bounds_noalloc", q, k)
     s = _shape(q)
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if out is not None:
+        _bounds_buffers("fsattn_head_bounds_noalloc", out, B, H, d)
+    _on_gpu("fsattn_head_bounds_noalloc", q, k, *((out.key_mean, out.rec) if out is not None else ()))
     if out is None:
         out = Bounds(torch.empty((B, H, d), dtype=torch.float32, device=q.device),
                      torch.empty((B, H, 8), dtype=torch.float32, device=q.device))
@@ -301,11 +348,13 @@ def noalloc_max_workspace() -> int:
     return lib().fsattn_head_bounds_noalloc_max_workspace()
 
 
-def _f32_ptr(t: Optional[torch.Tensor], shape, what: str) -> int:
+def _f32_ptr(t: Optional[torch.Tensor], shape, what: str, device: torch.device) -> int:
     if t is None:
         return 0
     if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
         raise FsattnError(1, f"{what} must be a contiguous float32 tensor of shape {tuple(shape)}")
+    if t.device != device:
+        raise FsattnError(1, f"{what} is on {t.device}, the operands on {device}")
     return t.data_ptr()
 
 
@@ -321,10 +370,17 @@ def produce(q_in: torch.Tensor, k_in: torch.Tensor, v_in: torch.Tensor, mask,
     values written. Inputs may be any [B, H, N, d] views with a contiguous
     last axis, e.g. slices of a token-major QKV projection output."""
     m = to_mask(mask)
+    _same_operands("fsattn_produce", q_in, k_in, v_in, *(out if out is not None else ()))
+    if out is not None and len(out) != 3:
+        raise FsattnError(1, "fsattn_produce: out holds Q, K and V")
     s = _shape(q_in)
     B, H, N, d = q_in.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if bounds is not None:
+        _bounds_buffers("fsattn_produce", bounds, B, H, d)
+    _on_gpu("fsattn_produce", q_in, k_in, v_in, workspace, *(out if out is not None else ()),
+            *((bounds.key_mean, bounds.rec) if bounds is not None else ()))
     L = lib()
     if out is None:
         out = tuple(torch.empty((B, H, N, d), dtype=q_in.dtype, device=q_in.device) for _ in range(3))
@@ -336,11 +392,12 @@ def produce(q_in: torch.Tensor, k_in: torch.Tensor, v_in: torch.Tensor, mask,
                         torch.empty((B, H, 8), dtype=torch.float32, device=q_in.device))
     q, k, v = out
     _check(L.fsattn_produce(_stream(q_in), ctypes.byref(s), ctypes.byref(m), _tensor(q_in), _tensor(k_in),
-                            _tensor(v_in), _f32_ptr(gamma_q, (H, d), "gamma_q"), _f32_ptr(gamma_k, (H, d), "gamma_k"),
-                            float(eps), _f32_ptr(rope_cos, (N, d // 2), "rope_cos"),
-                            _f32_ptr(rope_sin, (N, d // 2), "rope_sin"), _tensor(q), _tensor(k), _tensor(v),
-                            float(scale), float(threshold), bounds.key_mean.data_ptr(), bounds.rec.data_ptr(),
-                            workspace.data_ptr(), workspace.numel()), "fsattn_produce")
+                            _tensor(v_in), _f32_ptr(gamma_q, (H, d), "gamma_q", q_in.device),
+                            _f32_ptr(gamma_k, (H, d), "gamma_k", q_in.device), float(eps),
+                            _f32_ptr(rope_cos, (N, d // 2), "rope_cos", q_in.device),
+                            _f32_ptr(rope_sin, (N, d // 2), "rope_sin", q_in.device), _tensor(q), _tensor(k),
+                            _tensor(v), float(scale), float(threshold), bounds.key_mean.data_ptr(),
+                            bounds.rec.data_ptr(), workspace.data_ptr(), _nbytes(workspace)), "fsattn_produce")
     return q, k, v, bounds
 
 
@@ -382,10 +439,24 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dplan: DevicePlan
             out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
             lse: Optional[torch.Tensor] = None, stream: Optional[int] = None) -> torch.Tensor:
     """Attention over the plan's live blocks. Returns `out` ([B, H, N, d])."""
+    _same_operands("fsattn_forward", q, k, v)
     s = _shape(q)
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if out is not None:
+        if tuple(out.shape) != tuple(q.shape) or out.dtype not in (q.dtype, torch.float32):
+            raise FsattnError(1, f"fsattn_forward: out must be {tuple(q.shape)} of {q.dtype} or float32")
+    if bounds is not None:
+        _bounds_buffers("fsattn_forward", bounds, B, H, d)
+    if lse is not None:
+        _f32_buffer("fsattn_forward: lse", lse, B * H * N)
+    nqb, nnz = plan_size(dplan.mask)
+    for t, n, name in ((dplan.row_ptr, nqb + 1, "row_ptr"), (dplan.col_idx, nnz, "col_idx")):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() < n:
+            raise FsattnError(1, f"fsattn_forward: {name} must be a contiguous int32 tensor of {n} elements")
+    _on_gpu("fsattn_forward", q, k, v, out, lse, dplan.row_ptr, dplan.col_idx,
+            *((bounds.key_mean, bounds.rec) if bounds is not None else ()))
     if out is None:
         out = torch.empty((B, H, N, d), dtype=out_dtype or q.dtype, device=q.device)
     o_code = _dtype_code(out)
@@ -422,17 +493,22 @@ def prior_art_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask, s
     """The comparator (fsattn_prior_art_forward): the same attention with
     128-token tiles, window and reference-frame passes and a merge."""
     m = to_mask(mask)
+    _same_operands("fsattn_prior_art_forward", q, k, v)
     s = _shape(q)
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    if out is not None:
+        if tuple(out.shape) != tuple(q.shape) or out.dtype not in (q.dtype, torch.float32):
+            raise FsattnError(1, f"fsattn_prior_art_forward: out must be {tuple(q.shape)} of {q.dtype} or float32")
+    _on_gpu("fsattn_prior_art_forward", q, k, v, out, workspace)
     if out is None:
         out = torch.empty((B, H, N, d), dtype=out_dtype or q.dtype, device=q.device)
     need = prior_art_workspace_bytes(q, m)
-    if workspace is None or workspace.numel() < need:
+    if workspace is None or _nbytes(workspace) < need:
         workspace = torch.empty(max(1, need), dtype=torch.uint8, device=q.device)
     _check(lib().fsattn_prior_art_forward(stream if stream is not None else _stream(q), ctypes.byref(s),
                                           ctypes.byref(m), _tensor(q), _tensor(k), _tensor(v), _tensor(out),
-                                          _dtype_code(out), float(scale), workspace.data_ptr(), workspace.numel()),
+                                          _dtype_code(out), float(scale), workspace.data_ptr(), _nbytes(workspace)),
            "fsattn_prior_art_forward")
     return out

@@ -17,8 +17,10 @@
  * Conventions shared by every call:
  *  - Ownership: the caller owns every buffer, host or device. The library
  *    never allocates device memory and never synchronises a stream. Its
- *    only global state is a cache of launch choices per device and
- *    geometry (thread-safe).
+ *    global state: caches of launch choices per device and geometry, the
+ *    device address of fsattn_head_bounds_noalloc's workspace per device
+ *    (both thread-safe), and that workspace itself, a fixed array in the
+ *    library's code object on each device it runs on.
  *  - Errors: arguments are validated on the host before any launch. On any
  *    error nothing is launched and no output is written. A failed launch is
  *    reported as FSATTN_ERR_HIP. Device faults surface on the stream.

@@ -282,3 +282,47 @@ def test_produce_validates_on_host():
     assert call(shape=F.Shape(1, 2, 240, 96, 1)) == 3                   # head_dim not built
     assert call(shape=F.Shape(1, 2, 241, 64, 1)) == 1                   # seq_len != F*T
     assert call(mask=F.to_mask((5, 48, 1, 1, 0, 32, 16))) == 2
+
+
+def _cpu(shape=(1, 2, 240, 64), dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+def test_binding_rejects_operands_that_do_not_match_before_any_call():
+    """The binding checks what the C ABI cannot see: the operands' shapes,
+    dtypes, buffer extents and devices. Each bad case raises status 1, with
+    the message of its own check, before the library is asked to launch
+    anything (the tensors are CPU tensors, which the last check rejects)."""
+    import torch
+    mask = (3, 80, 1, 1, 0, 16, 16)
+    q = _cpu()
+    plan = fs.device_plan(mask, "cpu")
+    cases = [
+        ("dtype", lambda: fs.head_bounds(q, _cpu(dtype=torch.float32), mask)),
+        ("shape", lambda: fs.head_bounds(q, _cpu((1, 2, 160, 64)), mask)),
+        ("dtype", lambda: fs.head_bounds_noalloc(q, _cpu(dtype=torch.float32), mask)),
+        ("key_mean", lambda: fs.head_bounds(q, q, mask, out=fs.Bounds(torch.zeros(1, 2, 32), torch.zeros(1, 2, 8)))),
+        ("rec", lambda: fs.head_bounds_noalloc(q, q, mask, out=fs.Bounds(torch.zeros(1, 2, 64), torch.zeros(1, 2, 4)))),
+        ("shape", lambda: fs.forward(q, q, _cpu((1, 2, 240, 128)), plan, None)),
+        ("dtype", lambda: fs.forward(q, _cpu(dtype=torch.float32), q, plan, None)),
+        ("out must be", lambda: fs.forward(q, q, q, plan, None, out=_cpu((1, 2, 240, 32)))),
+        ("out must be", lambda: fs.forward(q, q, q, plan, None, out=_cpu(dtype=torch.float16))),
+        ("lse", lambda: fs.forward(q, q, q, plan, None, lse=torch.zeros(100, dtype=torch.float32))),
+        ("row_ptr", lambda: fs.forward(q, q, q, fs.DevicePlan(fs.to_mask(mask), torch.zeros(3, dtype=torch.int32),
+                                                              plan.col_idx), None)),
+        ("dtype", lambda: fs.produce(q, q, q, mask, out=(q, q, _cpu(dtype=torch.float32)))),
+        ("shape", lambda: fs.produce(q, _cpu((2, 2, 240, 64)), q, mask)),
+        ("key_mean", lambda: fs.produce(q, q, q, mask, bounds=fs.Bounds(torch.zeros(5), torch.zeros(1, 2, 8)))),
+        ("dtype", lambda: fs.prior_art_forward(q, _cpu(dtype=torch.float32), q, mask)),
+        ("out must be", lambda: fs.prior_art_forward(q, q, q, mask, out=_cpu((1, 1, 240, 64)))),
+        ("on a GPU", lambda: fs.head_bounds(q, q, mask)),
+        ("on a GPU", lambda: fs.head_bounds_noalloc(q, q, mask)),
+        ("on a GPU", lambda: fs.forward(q, q, q, plan, None)),
+        ("on a GPU", lambda: fs.produce(q, q, q, mask)),
+        ("on a GPU", lambda: fs.prior_art_forward(q, q, q, mask)),
+    ]
+    for what, call in cases:
+        with pytest.raises(fs.FsattnError, match=what) as e:
+            call()
+        assert e.value.status == 1, what
