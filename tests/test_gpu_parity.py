@@ -391,6 +391,18 @@ def test_forward_workload_parity(dev, config_inputs, i):
     assert torch.isfinite(o).all()
     vmax = torch.from_numpy(np.abs(v).max(axis=2, keepdims=True)).to(dev)
     assert bool((o.abs() <= vmax * (1 + 2 ** -7) + 1e-6).all())
+    # The log-sum-exp output, from a second launch that also writes it: O is
+    # bitwise the same, and every row's LSE is within the weights' rounding
+    # (LSE_TOL) plus the fp32 rounding of d-term logits, d 2^-24 scale |q| |k|.
+    out2, _, lse = _run(w, q, k, v, dev, lse=True)
+    assert torch.equal(out2, out)
+    _, ref_lse = _oracle_full(w, q, k, v)
+    qn = float(np.linalg.norm(q.astype(np.float64), axis=-1).max())
+    kn = float(np.linalg.norm(k.astype(np.float64), axis=-1).max())
+    tol = LSE_TOL[w.dtype] + w.head_dim * 2.0 ** -24 * qn * kn / math.sqrt(w.head_dim)
+    lerr = float(np.abs(lse.cpu().numpy() - ref_lse).max())
+    _say(f"    LSE max abs err {lerr:.3e} over every row (tol {tol:.2e})")
+    assert np.isfinite(lerr) and lerr <= tol, lerr
 
 
 def test_forward_fp32_workload_deterministic(dev, config_inputs):
@@ -501,6 +513,31 @@ def test_forward_deterministic(dev, config_inputs):
     d = fs.forward(qd, kd, vd, dp, bnd, flags=fs.make_flags("online"))
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(c, d)
+
+
+def test_binding_rejects_tensors_off_the_operands_gpu(dev):
+    """A CPU tensor beside GPU operands (K, V, the output, the workspace, the
+    plan or the angle tables) is rejected on the host with status 1, before
+    anything is launched."""
+    w = workloads.make_workload("devmix", 1, 2, 3, 80, 64, "bf16", 1, 1, 0, 16, 16)
+    q = torch.zeros((1, 2, 240, 64), dtype=torch.bfloat16, device=dev)
+    qc = q.cpu()
+    dp = fs.device_plan(w, dev)
+    bnd = fs.head_bounds(q, q, w)
+    calls = [
+        lambda: fs.head_bounds(q, qc, w),
+        lambda: fs.head_bounds(q, q, w, workspace=torch.empty(1 << 20, dtype=torch.uint8)),
+        lambda: fs.forward(q, q, qc, dp, bnd),
+        lambda: fs.forward(q, q, q, dp, bnd, out=torch.empty_like(qc)),
+        lambda: fs.forward(q, q, q, fs.device_plan(w, "cpu"), bnd),
+        lambda: fs.produce(q, q, q, w, rope_cos=torch.zeros(240, 32), rope_sin=torch.zeros(240, 32)),
+        lambda: fs.prior_art_forward(q, qc, q, w),
+    ]
+    for i, call in enumerate(calls):
+        with pytest.raises(fs.FsattnError) as e:
+            call()
+        assert e.value.status == 1, i
+    torch.cuda.synchronize()
 
 
 def test_mfma_probe_counts_and_runs(dev):
