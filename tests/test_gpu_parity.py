@@ -405,6 +405,63 @@ def test_forward_workload_parity(dev, config_inputs, i):
     assert np.isfinite(lerr) and lerr <= tol, lerr
 
 
+def _random_geometries(n, seed):
+    """Seeded random test-sized geometries: frames of 16-384 tokens, any
+    block sizes dividing them, windows of 0-3 frames on either side, no
+    reference frame or spans of 1-2 (global or not), head_dim 64 or 128,
+    bf16 or fp32, 1-2 batches and 1-3 heads, plain or offset keys."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        T = 16 * int(rng.integers(1, 25))
+        divs = [b for b in range(16, T + 1, 16) if T % b == 0]
+        F_ = int(rng.integers(1, 9))
+        ref = int(rng.integers(-1, F_))
+        rc = int(rng.integers(0, 3)) if ref >= 0 else 0
+        if ref + max(1, rc) > F_:
+            rc = 0
+        gq = int(rng.integers(0, 2)) if ref >= 0 else 0
+        out.append((f"rnd{i}", int(rng.integers(1, 3)), int(rng.integers(1, 4)), F_, T, int(rng.choice([64, 128])),
+                    "bf16" if rng.random() < 0.75 else "f32", int(rng.integers(0, 4)), int(rng.integers(0, 4)), ref,
+                    int(rng.choice(divs)), int(rng.choice(divs)), gq, rc, float(rng.choice([0.0, 1.5])),
+                    str(rng.choice(["auto", "online", "fixed"]))))
+    return out
+
+
+RANDOM_GEOMETRIES = _random_geometries(100, 2024)
+
+
+@pytest.mark.parametrize("case", RANDOM_GEOMETRIES, ids=[c[0] for c in RANDOM_GEOMETRIES])
+def test_forward_random_geometries(dev, case):
+    """Random geometries (seeded) in the library's default launch: the bound
+    records, every element of O and every row's LSE against the oracle.
+    "fixed" runs only where every head is eligible (else "auto")."""
+    w, q, k, v = _small(case[:12], seed=7, key_offset=case[14])
+    w = dataclasses.replace(w, ref_queries_global=case[12], ref_count=case[13])
+    _say(f"[fwd-random] {case}")
+    g = _geom(w)
+    td = _tdtype(w)
+    qd, kd, vd = (_to_dev(x, td, dev) for x in (q, k, v))
+    bnd = fs.head_bounds(qd, kd, w)
+    rec = bnd.host()
+    ref_b = oracle.head_bounds_ref(q, k, g)
+    for name, rname in (("q_norm_max", "q_max"), ("k_norm_max", "k_max"), ("gap_est", "gap_est")):
+        np.testing.assert_allclose(rec[name], ref_b[rname], rtol=1e-5, err_msg=name)
+    assert np.array_equal(rec["eligible"].astype(bool), ref_b["eligible"])
+    mode = case[15] if case[15] != "fixed" or rec["eligible"].all() else "auto"
+    lse = torch.empty((w.batch, w.heads, w.seq_len), dtype=torch.float32, device=dev)
+    out = fs.forward(qd, kd, vd, fs.device_plan(w, dev), bnd, flags=fs.make_flags(mode), lse=lse)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.attention_ref(q, k, v, g)
+    err = float(np.abs(out.float().cpu().numpy() - ref).max())
+    assert err <= TOL[w.dtype], err
+    qn = float(np.linalg.norm(q.astype(np.float64), axis=-1).max())
+    kn = float(np.linalg.norm(k.astype(np.float64), axis=-1).max())
+    tol = LSE_TOL[w.dtype] + w.head_dim * 2.0 ** -24 * qn * kn / math.sqrt(w.head_dim)
+    lerr = float(np.abs(lse.cpu().numpy() - ref_lse).max())
+    assert lerr <= tol, lerr
+
+
 def test_forward_fp32_workload_deterministic(dev, config_inputs):
     """The fp32 path on the 5 x 48 workload: two runs bitwise equal, in the
     default launch and forced online."""
