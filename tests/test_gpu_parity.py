@@ -718,6 +718,67 @@ def test_produce_parity(dev, case):
     assert torch.equal(bnd.rec, ref_b.rec) and torch.equal(bnd.key_mean, ref_b.key_mean)
 
 
+def _random_produce_cases(n, seed):
+    """Seeded random producer geometries: frames of 16-640 tokens (one to
+    five bounds chunks, the last one ragged), windows of 0-2 frames, no
+    reference frame or spans of 1-2 (global or not), head_dim 64 or 128,
+    bf16 or fp32, normalisation and rotation each on or off, in place or
+    into new tensors."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        F_ = int(rng.integers(1, 6))
+        ref = int(rng.integers(-1, F_))
+        rc = int(rng.integers(0, 3)) if ref >= 0 else 0
+        if ref + max(1, rc) > F_:
+            rc = 0
+        out.append((f"prnd{i}", int(rng.integers(1, 3)), int(rng.integers(1, 4)), F_, 16 * int(rng.integers(1, 41)),
+                    int(rng.choice([64, 128])), "bf16" if rng.random() < 0.7 else "f32", int(rng.integers(0, 3)),
+                    int(rng.integers(0, 3)), ref, int(rng.integers(0, 2)) if ref >= 0 else 0, rc,
+                    bool(rng.integers(0, 2)), bool(rng.integers(0, 2)), bool(rng.integers(0, 2))))
+    return out
+
+
+RANDOM_PRODUCE = _random_produce_cases(24, 77)
+
+
+@pytest.mark.parametrize("case", RANDOM_PRODUCE, ids=[c[0] for c in RANDOM_PRODUCE])
+def test_produce_random_geometries(dev, case):
+    """Random producer geometries (seeded): Q and K against produce_ref, V
+    copied exactly, the records equal bit for bit to fsattn_head_bounds on
+    the outputs, and within rtol 1e-5 of the oracle's on them."""
+    name, B, H, F_, T, d, dt, wb, wa, ref, gq, rc, norm, rope, in_place = case
+    _say(f"[produce-random] {case}")
+    w = workloads.make_workload(name, B, H, F_, T, d, dt, wb, wa, ref, 16, 16,
+                                ref_queries_global=gq, ref_count=rc)
+    x = workloads.make_producer_inputs(w, seed=9)
+    cos, sin = oracle.rope_tables_1d(w.seq_len, d)
+    cos, sin = cos.astype(np.float32), sin.astype(np.float32)
+    td = _tdtype(w)
+    qkv, views = _packed_views((x["q"], x["k"], x["v"]), td, dev)
+    gqt = torch.from_numpy(x["gamma_q"]).to(dev) if norm else None
+    gkt = torch.from_numpy(x["gamma_k"]).to(dev) if norm else None
+    tc = torch.from_numpy(cos).to(dev) if rope else None
+    ts = torch.from_numpy(sin).to(dev) if rope else None
+    q, k, v, bnd = fs.produce(*views, w, gqt, gkt, 1e-6, tc, ts, out=tuple(views) if in_place else None)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.produce_ref(x["q"], x["k"], x["v"], x["gamma_q"] if norm else None,
+                                    x["gamma_k"] if norm else None, 1e-6, cos if rope else None,
+                                    sin if rope else None)
+    qn, kn = q.float().cpu().numpy(), k.float().cpu().numpy()
+    for g, r, nm in ((qn, rq, "q"), (kn, rk, "k")):
+        assert np.all(np.abs(g - r) <= _produce_tol(dt, r)), (nm, np.abs(g - r).max())
+    assert np.array_equal(v.float().cpu().numpy(), rv)
+    ref_b = fs.head_bounds(q, k, w)
+    torch.cuda.synchronize()
+    assert torch.equal(bnd.rec, ref_b.rec) and torch.equal(bnd.key_mean, ref_b.key_mean)
+    got, orc = bnd.host(), oracle.head_bounds_ref(qn, kn, _geom(w))
+    for nm, rn in (("q_norm_max", "q_max"), ("k_norm_max", "k_max"), ("gap_est", "gap_est")):
+        np.testing.assert_allclose(got[nm], orc[rn], rtol=1e-5, err_msg=nm)
+    np.testing.assert_allclose(got["c_max"], orc["c_max"], rtol=1e-4, atol=1e-5 * float(orc["k_max"].max()))
+    assert np.array_equal(got["eligible"].astype(bool), orc["eligible"])
+
+
 def test_produce_then_forward_full_size(dev):
     """6 frames x 8160 tokens, 4 heads, d = 128, bf16 (the RMS-normalised
     workload's shape) from raw token-major projections: fsattn_produce
