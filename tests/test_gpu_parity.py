@@ -462,6 +462,45 @@ def test_forward_random_geometries(dev, case):
     assert lerr <= tol, lerr
 
 
+def test_offsets_past_2_31_elements(dev):
+    """Addressing at the largest sizes: 72 heads of 262144 tokens at d = 128
+    (16-token frames, each query sees its own frame only), 2.4e9 elements per
+    tensor, so the last heads start past 2^31 elements. The records of the
+    first and the last head (each computed whole on the host) and the O and
+    LSE rows of frames of both heads, near either end of the sequence,
+    against the oracle; each frame is its own problem, so a frame's slice is
+    checked with a one-frame geometry."""
+    B, H, F_, T, d = 1, 72, 16384, 16, 128
+    N = F_ * T
+    assert B * H * N * d > 2 ** 31
+    w = workloads.make_workload("offsets_2_31", B, H, F_, T, d, "bf16", 0, 0, -1, 16, 16)
+    _say("[big] drawing 3 x 2.4e9 bf16 inputs on the device")
+    q, k, v = (workloads.device_normal((B, H, N, d), s, dev, torch.bfloat16) for s in (31, 32, 33))
+    bnd = fs.head_bounds(q, k, w)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    _say("[big] forward")
+    out = fs.forward(q, k, v, fs.plan_on_device(w, dev), bnd, lse=lse)
+    torch.cuda.synchronize()
+    rec = bnd.host()
+    for h in (0, H - 1):
+        qh, kh = (t[:, h:h + 1].float().cpu().numpy() for t in (q, k))
+        ref = oracle.head_bounds_ref(qh, kh, _geom(w))
+        np.testing.assert_allclose(bnd.key_mean[:, h].cpu().numpy(), ref["mu"][:, 0], rtol=1e-5, atol=1e-6)
+        for name, rname in (("q_norm_max", "q_max"), ("k_norm_max", "k_max"), ("gap_est", "gap_est")):
+            np.testing.assert_allclose(rec[name][:, h], ref[rname][:, 0], rtol=1e-5, err_msg=f"{name} head {h}")
+        assert bool(rec["eligible"][0, h]) == bool(ref["eligible"][0, 0])
+    g1 = oracle.MaskGeometry(1, T, 0, 0, -1, 16, 16)
+    for h in (0, H - 1):
+        for f in (0, 1, F_ // 2, F_ - 2, F_ - 1):
+            sl = slice(f * T, (f + 1) * T)
+            qs, ks, vs = (t[:, h:h + 1, sl].float().cpu().numpy() for t in (q, k, v))
+            ro, rl = oracle.attention_ref(qs, ks, vs, g1)
+            assert np.abs(out[:, h:h + 1, sl].float().cpu().numpy() - ro).max() <= TOL["bf16"], (h, f)
+            assert np.abs(lse[:, h:h + 1, sl].cpu().numpy() - rl).max() <= LSE_TOL["bf16"], (h, f)
+    del q, k, v, out, lse, bnd
+    torch.cuda.empty_cache()
+
+
 def test_forward_fp32_workload_deterministic(dev, config_inputs):
     """The fp32 path on the 5 x 48 workload: two runs bitwise equal, in the
     default launch and forced online."""

@@ -170,3 +170,20 @@ def make_producer_inputs(w: Workload, seed: int = 0):
         q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
     return dict(q=q, k=k, v=v, gamma_q=gq, gamma_k=gk,
                 cos=np.cos(ang).astype(np.float32), sin=np.sin(ang).astype(np.float32))
+
+
+def device_normal(shape, seed: int, device, dtype):
+    """Standard-normal values drawn on `device` by torch's seeded generator,
+    one [.., N, d] slab per (batch, head) in order, each rounded to `dtype`:
+    inputs too large to draw on the host (addressing tests past 2^31
+    elements). Both the GPU path and the oracle read the same tensor, the
+    oracle through host copies of slices of it."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    B, H = shape[0], shape[1]
+    x = torch.empty(shape, dtype=dtype, device=device)
+    for b in range(B):
+        for h in range(H):
+            x[b, h] = torch.randn(shape[2:], generator=g, device=device, dtype=torch.float32).to(dtype)
+    return x
