@@ -326,3 +326,29 @@ def test_binding_rejects_operands_that_do_not_match_before_any_call():
         with pytest.raises(fs.FsattnError, match=what) as e:
             call()
         assert e.value.status == 1, what
+
+
+def test_empty_inputs_are_rejected_by_every_entry_point():
+    """Empty problems (no batch, no head, no frame, no token) are argument or
+    geometry errors at every GPU entry point, before anything is launched;
+    the workspace queries return 0 for them."""
+    L = fs.lib()
+    m = F.to_mask((5, 48, 1, 1, 0, 16, 16))
+    t = _t()
+    for s in (F.Shape(0, 2, 240, 64, 1), F.Shape(1, 0, 240, 64, 1), F.Shape(1, 2, 0, 64, 1)):
+        assert L.fsattn_head_bounds_workspace_bytes(ctypes.byref(s), ctypes.byref(m)) == 0
+        assert L.fsattn_prior_art_workspace_bytes(ctypes.byref(s), ctypes.byref(m)) == 0
+        assert _bounds_call(shape=s) in (1, 2)
+        assert L.fsattn_head_bounds_noalloc(None, ctypes.byref(s), ctypes.byref(m), t, t, 0.125, 30.0,
+                                            FAKE, FAKE) in (1, 2)
+        assert _fwd_call(shape=s) in (1, 2)
+        assert L.fsattn_produce(None, ctypes.byref(s), ctypes.byref(m), t, t, t, None, None, 1e-6, None, None,
+                                t, t, t, 0.125, 30.0, FAKE, FAKE, FAKE, 1 << 30) in (1, 2)
+        assert L.fsattn_prior_art_forward(None, ctypes.byref(s), ctypes.byref(m), t, t, t, t, 1, 0.125,
+                                          FAKE, 1 << 30) in (1, 2)
+    for empty in ((0, 48, 1, 1, 0, 16, 16), (5, 0, 1, 1, 0, 16, 16)):
+        me = F.to_mask(empty)
+        nq, nz = ctypes.c_int64(), ctypes.c_int64()
+        assert L.fsattn_plan_size(ctypes.byref(me), ctypes.byref(nq), ctypes.byref(nz)) == 2
+        assert _bounds_call(mask=me) == 2
+        assert _fwd_call(mask=me) == 2
