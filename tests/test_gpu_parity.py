@@ -501,6 +501,46 @@ def test_offsets_past_2_31_elements(dev):
     torch.cuda.empty_cache()
 
 
+def test_whole_path_in_a_captured_graph(dev):
+    """Plan (device), bounds and forward captured once in a HIP graph (the
+    path records no memset and allocates nothing: every buffer is the
+    caller's) and replayed three times; before each replay new inputs are
+    copied in eagerly and the device synchronised; every replay's output,
+    records and LSE equal an eager run's on the same inputs, bit for bit."""
+    w = workloads.make_workload("graph_path", 1, 4, 6, 480, 128, "bf16", 1, 1, 0, 48, 80)
+    sets = []
+    for seed in (21, 22, 23, 24):
+        q, k, v = workloads.make_inputs(w, seed=seed)
+        sets.append(tuple(_to_dev(x, torch.bfloat16, dev) for x in (q, k, v)))
+    qs, ks, vs = (t.clone() for t in sets[0])
+    dp = fs.plan_on_device(w, dev)
+    ws = torch.empty(fs.head_bounds_workspace_bytes(qs, w), dtype=torch.uint8, device=dev)
+    bnd = fs.head_bounds(qs, ks, w, workspace=ws)
+    out = torch.empty_like(qs)
+    lse = torch.empty((w.batch, w.heads, w.seq_len), dtype=torch.float32, device=dev)
+    fs.forward(qs, ks, vs, dp, bnd, out=out, lse=lse)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fs.plan_on_device(w, out=dp)
+        fs.head_bounds(qs, ks, w, workspace=ws, out=bnd)
+        fs.forward(qs, ks, vs, dp, bnd, out=out, lse=lse)
+    torch.cuda.synchronize()
+    for rep, (q, k, v) in enumerate(sets[1:]):
+        _say(f"[graph-path] replay {rep}")
+        for dst, src in ((qs, q), (ks, k), (vs, v)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        rb = fs.head_bounds(q, k, w)
+        rl = torch.empty_like(lse)
+        ro = fs.forward(q, k, v, fs.plan_on_device(w, dev), rb, lse=rl)
+        torch.cuda.synchronize()
+        assert torch.equal(bnd.rec, rb.rec) and torch.equal(bnd.key_mean, rb.key_mean), rep
+        assert torch.equal(out, ro) and torch.equal(lse, rl), rep
+
+
 def test_forward_fp32_workload_deterministic(dev, config_inputs):
     """The fp32 path on the 5 x 48 workload: two runs bitwise equal, in the
     default launch and forced online."""
