@@ -372,14 +372,20 @@ __global__ __launch_bounds__(kThreads) void bounds_pass2(BoundsParams p) {
 }
 
 // Per head: max |k - mu| from the chunk maxima, then the bound, the gap
-// estimate and eligibility.
+// estimate and eligibility. A key mean that is not finite (a key that is
+// not) leaves the fixed shift without meaning, and the maxima skip NaN, so
+// such a head is marked not eligible: the online path then confines the
+// non-finite values to the rows that attend to them.
 __global__ __launch_bounds__(kThreads) void bounds_final(BoundsParams p) {
   __shared__ float red[kThreads / 64];
   const int bh = blockIdx.x;
   const int NC = p.F * p.chunks_per_frame;
   float km = 0.f;
   for (int c = threadIdx.x; c < NC; c += kThreads) km = fmaxf(km, p.ws_kmax[(int64_t)bh * NC + c]);
+  float bad = 0.f;
+  for (int j = threadIdx.x; j < p.D; j += kThreads) bad = isfinite(p.key_mean[(int64_t)bh * p.D + j]) ? bad : 1.f;
   km = block_max<kThreads>(km, red);
+  bad = block_max<kThreads>(bad, red);
   if (threadIdx.x == 0) {
     fsattn_head_bound r = p.rec[bh];   // q_norm_max and c_max from the head pass
     const float qn = r.q_norm_max, cn = r.c_max;
@@ -387,7 +393,7 @@ __global__ __launch_bounds__(kThreads) void bounds_final(BoundsParams p) {
     r.k_norm_max = kn;
     r.bound = p.scale * qn * kn;
     r.gap_est = p.scale * qn * (kn + cn);
-    r.eligible = r.gap_est <= p.threshold ? 1 : 0;
+    r.eligible = r.gap_est <= p.threshold && bad == 0.f ? 1 : 0;
     r.pad[0] = r.pad[1] = 0;
     p.rec[bh] = r;
   }

@@ -118,7 +118,8 @@ typedef struct fsattn_tensor {
  *                (Cauchy-Schwarz: >= scale * q_i . (k_j - mu) for all i, j)
  *   gap_est    = scale * q_norm_max * (k_norm_max + c_max)
  *                (>= bound minus the largest live logit of every row)
- *   eligible   = gap_est <= gap_threshold_nats (1) or not (0)
+ *   eligible   = gap_est <= gap_threshold_nats and the key mean finite (1)
+ *                or not (0)
  * 32 bytes, naturally aligned.
  */
 typedef struct fsattn_head_bound {
@@ -212,6 +213,12 @@ size_t fsattn_head_bounds_workspace_bytes(const fsattn_shape *s, const fsattn_ma
  * (>= fsattn_head_bounds_workspace_bytes). Reductions run in a fixed order
  * without atomics: results are bitwise reproducible. scale > 0;
  * gap_threshold_nats >= 0. Asynchronous on hip_stream.
+ * Inputs are meant to be finite. If they are not, the effect stays in the
+ * head and, through fsattn_forward, in the rows that touch the value: the
+ * norm maxima skip NaN (a NaN query row leaves the record as if the row
+ * were absent; that row's output is NaN), and a head whose key mean is not
+ * finite (a non-finite key) is marked not eligible, so the online path
+ * confines the damage to the rows that attend to that key.
  * Errors: INVALID_ARGUMENT, BLOCK_GEOMETRY, UNSUPPORTED,
  * BUFFER_TOO_SMALL (workspace), HIP.
  */

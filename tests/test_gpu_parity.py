@@ -541,6 +541,48 @@ def test_whole_path_in_a_captured_graph(dev):
         assert torch.equal(out, ro) and torch.equal(lse, rl), rep
 
 
+@pytest.mark.parametrize("where", ["q", "k"])
+def test_non_finite_input_stays_in_the_rows_it_touches(dev, where):
+    """A NaN at query (or key) 77 of head 1 of four 64-token frames (window
+    +-1, reference frame 0): the other heads' records and outputs equal
+    those of the same call without it, bit for bit; in head 1 every row that
+    does not touch the NaN matches the oracle on the clean inputs. A NaN
+    query leaves head 1 eligible (the norm maximum skips it) and only its own
+    row non-finite; a NaN key makes the key mean non-finite, so head 1 is not
+    eligible and only the rows that attend to frame 1 are non-finite (frame
+    3's rows see frames 2, 3 and 0 and stay exact)."""
+    w = workloads.make_workload("nan_head", 1, 3, 4, 64, 128, "bf16", 1, 1, 0, 32, 32)
+    q, k, v = workloads.make_inputs(w, seed=5)
+    qd, kd, vd = (_to_dev(x, torch.bfloat16, dev) for x in (q, k, v))
+    dp = fs.device_plan(w, dev)
+    b0 = fs.head_bounds(qd, kd, w)
+    o0 = fs.forward(qd, kd, vd, dp, b0)
+    bad = (qd if where == "q" else kd).clone()
+    bad[0, 1, 77, 5] = float("nan")
+    q1, k1 = (bad, kd) if where == "q" else (qd, bad)
+    b1 = fs.head_bounds(q1, k1, w)
+    o1 = fs.forward(q1, k1, vd, dp, b1)
+    torch.cuda.synchronize()
+    assert b0.host()["eligible"].all()
+    for h in (0, 2):
+        assert torch.equal(b1.rec[0, h], b0.rec[0, h]) and torch.equal(b1.key_mean[0, h], b0.key_mean[0, h])
+        assert torch.equal(o1[0, h], o0[0, h])
+    ref, _ = oracle.attention_ref(q, k, v, _geom(w))
+    got = o1[0, 1].float().cpu().numpy()
+    if where == "q":
+        assert b1.host()["eligible"][0, 1] == 1
+        clean = np.ones(w.seq_len, bool)
+        clean[77] = False
+        assert not np.isfinite(got[77]).all()
+    else:
+        assert b1.host()["eligible"][0, 1] == 0
+        clean = np.zeros(w.seq_len, bool)
+        clean[192:] = True                       # frame 3: frames 2, 3 and the reference frame 0
+        assert (~np.isfinite(got[:192])).any(axis=1).all()   # frames 0-2 all attend to key 77
+    assert np.isfinite(got[clean]).all()
+    assert np.abs(got[clean] - ref[0, 1][clean]).max() <= TOL["bf16"]
+
+
 def test_forward_fp32_workload_deterministic(dev, config_inputs):
     """The fp32 path on the 5 x 48 workload: two runs bitwise equal, in the
     default launch and forced online."""
