@@ -583,6 +583,61 @@ def test_non_finite_input_stays_in_the_rows_it_touches(dev, where):
     assert np.abs(got[clean] - ref[0, 1][clean]).max() <= TOL["bf16"]
 
 
+def _random_shaped_cases(n, seed):
+    """Seeded random bf16 geometries, each with a random launch-shape
+    override (waves and rows per wave from every built shape, keys per step
+    and ring depth, tile dealing), so that ragged last waves, remainder steps
+    and idle waves meet every shape."""
+    rng = np.random.default_rng(seed)
+    steps = [(32, 2), (32, 3), (32, 4), (64, 2)]
+    out = []
+    for i in range(n):
+        T = 16 * int(rng.integers(1, 21))
+        divs = [b for b in range(16, T + 1, 16) if T % b == 0]
+        F_ = int(rng.integers(1, 7))
+        ref = int(rng.integers(-1, F_))
+        rc = int(rng.integers(0, 3)) if ref >= 0 else 0
+        if ref + max(1, rc) > F_:
+            rc = 0
+        waves, rows = SHAPES[int(rng.integers(0, len(SHAPES)))]
+        kstep, ring = steps[int(rng.integers(0, len(steps)))]
+        out.append((f"shp{i}", int(rng.integers(1, 3)), int(rng.integers(1, 4)), F_, T, int(rng.choice([64, 128])),
+                    "bf16", int(rng.integers(0, 3)), int(rng.integers(0, 3)), ref, int(rng.choice(divs)),
+                    int(rng.choice(divs)), int(rng.integers(0, 2)) if ref >= 0 else 0, rc, waves, rows, kstep, ring,
+                    int(rng.integers(0, 5)), str(rng.choice(["auto", "online", "fixed"]))))
+    return out
+
+
+RANDOM_SHAPED = _random_shaped_cases(48, 4096)
+
+
+@pytest.mark.parametrize("case", RANDOM_SHAPED, ids=[c[0] for c in RANDOM_SHAPED])
+def test_forward_random_geometries_any_launch_shape(dev, case):
+    """Every element of O and every LSE row against the oracle for a random
+    geometry in a random launch shape ("fixed" only where every head is
+    eligible, else "auto")."""
+    waves, rows, kstep, ring, deal, mode = case[14:]
+    w, q, k, v = _small(case[:12], seed=8, key_offset=1.5)
+    w = dataclasses.replace(w, ref_queries_global=case[12], ref_count=case[13])
+    _say(f"[fwd-random-shape] {case}")
+    qd, kd, vd = (_to_dev(x, torch.bfloat16, dev) for x in (q, k, v))
+    bnd = fs.head_bounds(qd, kd, w)
+    if mode == "fixed" and not bnd.host()["eligible"].all():
+        mode = "auto"
+    flags = fs.make_flags(mode, waves=waves, rows_per_wave=rows, key_step=kstep, ring=ring, deal=deal)
+    assert fs.launch_info(tuple(qd.shape), fs.BF16, w, flags)[:3] == (waves, rows, kstep)
+    lse = torch.empty((w.batch, w.heads, w.seq_len), dtype=torch.float32, device=dev)
+    out = fs.forward(qd, kd, vd, fs.device_plan(w, dev), bnd, flags=flags, lse=lse)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.attention_ref(q, k, v, _geom(w))
+    err = float(np.abs(out.float().cpu().numpy() - ref).max())
+    assert err <= TOL["bf16"], err
+    qn = float(np.linalg.norm(q.astype(np.float64), axis=-1).max())
+    kn = float(np.linalg.norm(k.astype(np.float64), axis=-1).max())
+    tol = LSE_TOL["bf16"] + w.head_dim * 2.0 ** -24 * qn * kn / math.sqrt(w.head_dim)
+    assert float(np.abs(lse.cpu().numpy() - ref_lse).max()) <= tol
+
+
 def test_forward_fp32_workload_deterministic(dev, config_inputs):
     """The fp32 path on the 5 x 48 workload: two runs bitwise equal, in the
     default launch and forced online."""
